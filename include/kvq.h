@@ -1,0 +1,211 @@
+/*
+ * kvq.h — C ABI of libkvq: a quantized paged KV cache and paged-attention
+ * decode over it, for AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are (pages cited by title and section):
+ *   - vLLM issue 4025 "[Feature]: Support for 4-bit KV Cache in paged-attention
+ *     op", section "methods": (1) compute the quantisation scale and zero point
+ *     and convert an existing fp16/bf16 KV cache; (2) store quantised KV in the
+ *     paged-cache write; (3) paged attention that takes optional k_scale,
+ *     k_zeropoint, v_scale, v_zeropoint, converts the stored codes back to 16-bit
+ *     and computes.
+ *   - vLLM PR 4893 "[Misc] Load FP8 kv-cache scaling factors from checkpoints",
+ *     description items 1-2: KV dtypes auto (= the model's 16-bit type), fp8
+ *     (= e4m3), fp8_e4m3, fp8_e5m2; a scale of 1.0 when none is supplied.
+ *   - "vllm-int8-kv-cache-for-ampere-sm86" summary: an INT8 KV cache with
+ *     per-layer scaling values calibrated offline; FP8-E4M3 for one part of
+ *     the cache (here: K and V dtypes are independent).
+ *   - modelium "vLLM FP8 KV-кеш: калибровка и проверка памяти и качества",
+ *     scale schemes: per-tensor and per-attention-head scales.
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are HIP device pointers, (host) host pointers.
+ *     The caller allocates and owns every buffer, including decode workspace;
+ *     the library allocates nothing, keeps no pointer past the call and no state
+ *     between calls, and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns without synchronising; buffers must stay
+ *     valid until that work has run.
+ *   - Argument checks run on the host before any HIP call and return a status;
+ *     nothing is enqueued on error.  KVQ_ERR_HIP reports a failed launch.
+ *   - Bad data found on the device never faults: out-of-range slots or block
+ *     ids are skipped (their contribution is treated as absent) and, when
+ *     `err_count` (device int32, nullable) is given, counted into it with an
+ *     atomic add.  The caller zeroes *err_count when it wants a fresh count.
+ *   - bf16 inputs are passed as uint16_t bit patterns, row-major, contiguous,
+ *     16-byte aligned.
+ *
+ * Paged cache layout (one layer):
+ *   pages  [num_blocks][num_kv_heads][block_size][row_bytes], row_bytes =
+ *          2*head_dim (BF16), head_dim (INT8 / FP8), head_dim/2 (INT4: two codes
+ *          per byte, the even element in the low nibble)
+ *   slot   block * block_size + offset
+ *   INT4 metadata [num_blocks][num_kv_heads][block_size][2] float32 =
+ *          (scale, zero_point) per (token, KV head); x_hat = (q - zp) * scale.
+ *   Scales of INT8 / FP8: float32 [1] (per tensor) or [num_kv_heads] (per KV
+ *          head); x_hat = code * scale (FP8: decoded value * scale).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  KVQ_ERR_UNSUPPORTED = 3, /* dtype, granularity or head_dim not supported */
+  KVQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
+  KVQ_ERR_HIP = 6          /* a HIP launch failed */
+} kvq_status;
+
+/* Element formats.  KVQ_BF16 is the "auto" (unquantised) cache; KVQ_FP8_E4M3 is
+ * what "fp8" means.  FP8 is the OCP 8-bit format (e4m3: no infinities, max 448;
+ * e5m2: max 57344).  KVQ_F32 is valid only as a decode output type. */
+typedef enum kvq_dtype {
+  KVQ_BF16 = 0,
+  KVQ_INT8 = 1,
+  KVQ_FP8_E4M3 = 2,
+  KVQ_FP8_E5M2 = 3,
+  KVQ_INT4_ASYM = 4,
+  KVQ_F32 = 5
+} kvq_dtype;
+
+typedef enum kvq_granularity {
+  KVQ_PER_TENSOR = 0,     /* one scale for the whole K (or V) cache */
+  KVQ_PER_KV_HEAD = 1,    /* one scale per KV head */
+  KVQ_PER_TOKEN_HEAD = 2  /* INT4 only: (scale, zero point) per (token, KV head) */
+} kvq_granularity;
+
+/* Describes one layer's paged cache.  A host struct read during the call only. */
+typedef struct kvq_cache {
+  int32_t k_dtype, v_dtype;       /* kvq_dtype, independent (e.g. K e4m3, V int8) */
+  int32_t k_gran, v_gran;         /* kvq_granularity (ignored for BF16) */
+  int32_t num_blocks;             /* pages in the pool */
+  int32_t block_size;             /* tokens per page; must be 16 */
+  int32_t num_kv_heads;           /* >= 1 */
+  int32_t head_dim;               /* 64 or 128 */
+  void* k_pages;                  /* (device) K pages, layout above, 16-B aligned */
+  void* v_pages;                  /* (device) V pages */
+  const float* k_scale;           /* (device) [1] or [num_kv_heads]; NULL = 1.0; INT8/FP8 only */
+  const float* v_scale;           /* (device) idem for V */
+  float* k_meta;                  /* (device) INT4 (scale, zero point) metadata, else unused */
+  float* v_meta;
+} kvq_cache;
+
+/*
+ * kvq_calibrate_scales — absmax scale calibration (a running maximum).
+ *
+ * The sm86 INT8 summary calibrates per-layer scaling values offline; the
+ * modelium FP8 page names per-tensor and per-attention-head scales.  For each
+ * group (the whole tensor, or all tokens x head_dim of one KV head):
+ *     absmax_inout[g] = max(absmax_inout[g], max |x|)     (NaN ignored)
+ *     scale_out[g]    = absmax_inout[g] / qmax             (IEEE division)
+ *                       or 1.0 when absmax_inout[g] == 0
+ * with qmax = 127 (KVQ_INT8), 448 (KVQ_FP8_E4M3), 57344 (KVQ_FP8_E5M2).
+ *   x            (device) bf16 [num_tokens][num_kv_heads][head_dim]
+ *   granularity  KVQ_PER_TENSOR (G = 1) or KVQ_PER_KV_HEAD (G = num_kv_heads)
+ *   absmax_inout (device) float32 [G]; the caller zero-fills it before the first
+ *                batch and passes it again to accumulate over batches
+ *   scale_out    (device) float32 [G], rewritten on every call
+ * num_tokens may be 0 (scale_out is then recomputed from absmax_inout alone).
+ */
+kvq_status kvq_calibrate_scales(const uint16_t* x, int64_t num_tokens, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t granularity, int32_t target_dtype,
+                                float* absmax_inout, float* scale_out, void* stream);
+
+/*
+ * kvq_cache_write — fused quantise-and-scatter of new K/V rows into the pages.
+ *
+ * vLLM issue 4025, methods item 2.  Row i of k_new / v_new is encoded and stored
+ * at slot_mapping[i]:
+ *   INT8:  q = clamp(RNE(x / s), -127, 127)            (NaN -> 0)
+ *   FP8:   nearest code of x / s, ties to even, saturating to the largest finite
+ *          value (NaN -> a NaN code)
+ *   INT4:  per row: s = (max - min) / 15, zp = RNE(-min / s) (s = |min| or 1 for
+ *          a constant row), q = clamp(RNE(x / s) + zp, 0, 15); (s, zp) stored
+ *          in the metadata
+ *   BF16:  copied
+ * x / s is an IEEE-correctly-rounded float32 division.
+ *   k_new, v_new  (device) bf16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  (device) int64 [num_tokens]; < 0 skips the row; >= num_blocks *
+ *                 block_size is skipped and counted in err_count
+ *   num_tokens    >= 0
+ */
+kvq_status kvq_cache_write(const kvq_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens, int32_t* err_count,
+                           void* stream);
+
+/*
+ * kvq_convert_cache — convert an existing bf16 paged cache into `dst`'s format.
+ *
+ * vLLM issue 4025, methods item 1.  Every slot of blocks [first_block,
+ * first_block + num_blocks) of the bf16 source pages (same geometry as dst, row
+ * bytes 2*head_dim) is encoded as kvq_cache_write would encode it and stored at
+ * the same slot of dst.  For INT8 / FP8 dst's scales must be set (calibrate first).
+ *   k_src, v_src (device) bf16 [dst->num_blocks][num_kv_heads][block_size][head_dim]
+ */
+kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const uint16_t* v_src,
+                             int32_t first_block, int32_t num_blocks, void* stream);
+
+/*
+ * kvq_decode_workspace_size — bytes of device workspace kvq_paged_attention_decode
+ * needs for these sizes (0 when every sequence fits one partition).
+ * partition = 0 selects the default (512 tokens).
+ */
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition);
+
+/*
+ * kvq_paged_attention_decode — one query token per sequence against the paged
+ * quantised cache.
+ *
+ * vLLM issue 4025, methods item 3 (attention over the stored codes with their
+ * scales / zero points) and vLLM PR 4893's note that decode runs a paged
+ * attention kernel.  For sequence b and query head h (KV head h / (Hq/Hkv)):
+ *     z_i = softmax_scale * sum_c q[b][h][c] * k_hat_i[c]    for i < seq_lens[b]
+ *     out[b][h] = sum_i softmax(z)_i * v_hat_i
+ * Token position p of sequence b is read from page block_tables[b][p / 16],
+ * offset p % 16.  Accumulation is float32.  Sequences are cut into partitions of
+ * `partition` tokens (0 = 512); when max_seq_len exceeds it, per-partition
+ * (max, sum, accumulator) go to the workspace and a reduce pass merges them.
+ *   q             (device) bf16 [batch][num_q_heads][head_dim]; |q| < 65504
+ *   block_tables  (device) int32 [batch][max_blocks_per_seq]
+ *   seq_lens      (device) int32 [batch]; <= 0 gives a zero output row; values
+ *                 above max_seq_len or max_blocks_per_seq*16 are clamped and counted
+ *   max_seq_len   host-side upper bound of seq_lens (sizes the launch)
+ *   num_q_heads   multiple of num_kv_heads, at most 16 query heads per KV head
+ *   partition     0 or a positive multiple of 16
+ *   workspace     (device) >= kvq_decode_workspace_size(...) bytes, 16-B aligned;
+ *                 may be NULL when that size is 0
+ *   out_dtype     KVQ_BF16 (round to nearest even) or KVQ_F32
+ *   out           (device) [batch][num_q_heads][head_dim] of out_dtype
+ * Supported K/V dtype pairs: any of {INT8, FP8_E4M3, FP8_E5M2, BF16} for K and for
+ * V independently, and INT4 for both.
+ */
+kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                      void* workspace, size_t workspace_bytes, int32_t out_dtype,
+                                      void* out, int32_t* err_count, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kvq_status_string(int32_t status);
+
+/* KVQ_ABI_VERSION of the built library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

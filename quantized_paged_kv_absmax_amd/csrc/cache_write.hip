@@ -1,0 +1,182 @@
+// cache_write.hip — fused quantise-and-scatter of K/V rows into the paged cache
+// (vLLM issue 4025, methods item 2) and conversion of an existing bf16 paged
+// cache (methods item 1).
+//
+// One row = head_dim bf16 values of one (token, KV head).  A row is handled by
+// D/8 consecutive lanes, each loading 16 bytes (8 values) and storing 8 codes
+// (8 bytes; 4 bytes for INT4).  INT4 finds the row's min / max with xor
+// shuffles inside the lane group, and the group's first lane stores the
+// (scale, zero point) pair.  Blocks in y = 0 encode K, y = 1 encode V, so a
+// launch streams both tensors; the element format is a per-launch switch that
+// is uniform across the grid.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct RowSide {
+  const uint16_t* src;      // bf16 rows
+  uint8_t* pages;
+  const float* scale;       // [1] or [Hkv] or null
+  int scale_per_head;
+  float* meta;              // int4 (scale, zp)
+  int dtype;
+};
+
+// Encode the 8 values this lane holds (x[0..7], elements [8*j, 8*j+8) of the row)
+// and store them into the destination row.
+template <int D, int LPR>
+__device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, float s,
+                                             uint8_t* dst_row, float* meta_row, int j) {
+  if (dtype == DT_BF16) {
+    // unreachable: bf16 rows are copied by the caller
+    return;
+  }
+  if (dtype == DT_INT4) {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    float sc = (mx - mn) / 15.0f;
+    if (sc == 0.0f || !(fabsf(sc) <= 3.402823466e38f)) sc = (mn != 0.0f) ? fabsf(mn) : 1.0f;
+    const float zp = rintf(-mn / sc);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = rintf(x[i] / sc) + zp;
+      q = fminf(fmaxf(q, 0.0f), 15.0f);
+      packed |= ((uint32_t)q) << (4 * i);
+    }
+    *reinterpret_cast<uint32_t*>(dst_row + 4 * j) = packed;
+    if (j == 0) *reinterpret_cast<float2*>(meta_row) = make_float2(sc, zp);
+    return;
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t c;
+    if (dtype == DT_INT8) c = enc_int8(x[i], s);
+    else if (dtype == DT_E4M3) c = enc_fp8<DT_E4M3>(x[i], s);
+    else c = enc_fp8<DT_E5M2>(x[i], s);
+    if (i < 4) lo |= c << (8 * i); else hi |= c << (8 * (i - 4));
+  }
+  *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
+}
+
+template <int D>
+__device__ __forceinline__ void process_row(const RowSide& sd, const uint16_t* src_row, int64_t dst_row_idx,
+                                            int h, int j) {
+  constexpr int LPR = D / 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src_row + 8 * j);
+  if (sd.dtype == DT_BF16) {
+    *reinterpret_cast<uint4*>(sd.pages + dst_row_idx * (2 * D) + 16 * j) = raw;
+    return;
+  }
+  float x[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+  float s = 1.0f;
+  if (sd.scale) s = sd.scale[sd.scale_per_head ? h : 0];
+  const int rb = (sd.dtype == DT_INT4) ? D / 2 : D;
+  encode_store<D, LPR>(x, sd.dtype, s, sd.pages + dst_row_idx * rb,
+                       sd.meta ? sd.meta + dst_row_idx * 2 : nullptr, j);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSide v, const int64_t* slots,
+                                                               int64_t T, int Hkv, int64_t num_slots,
+                                                               int32_t* err) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;  // rows per block
+  const RowSide& sd = (blockIdx.y == 0) ? k : v;
+  const int j = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  if (row >= T * Hkv) return;
+  const int64_t t = row / Hkv;
+  const int h = (int)(row % Hkv);
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  if (slot >= num_slots) {
+    if (err && blockIdx.y == 0 && h == 0 && j == 0) atomicAdd(err, 1);
+    return;
+  }
+  const int64_t blk = slot / 16, off = slot % 16;
+  const int64_t dst = (blk * Hkv + h) * 16 + off;
+  process_row<D>(sd, sd.src + row * D, dst, h, j);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v, int first_block, int n_blocks,
+                                                           int Hkv) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;
+  const RowSide& sd = (blockIdx.y == 0) ? k : v;
+  const int j = threadIdx.x % LPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // row within the block range
+  if (r >= (int64_t)n_blocks * Hkv * 16) return;
+  const int64_t dst = (int64_t)first_block * Hkv * 16 + r;          // same slot in source and dest
+  const int h = (int)((dst / 16) % Hkv);
+  process_row<D>(sd, sd.src + dst * D, dst, h, j);
+}
+
+RowSide side(const CacheView& c, bool is_k, const uint16_t* src) {
+  RowSide s;
+  s.src = src;
+  s.pages = is_k ? c.k_pages : c.v_pages;
+  s.scale = is_k ? c.k_scale : c.v_scale;
+  s.scale_per_head = (is_k ? c.k_gran : c.v_gran) == 1;
+  s.meta = is_k ? c.k_meta : c.v_meta;
+  s.dtype = is_k ? c.k_dtype : c.v_dtype;
+  return s;
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const uint16_t* v_new,
+                              const int64_t* slots, int64_t T, int32_t* err, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const RowSide k = side(c, true, k_new), v = side(c, false, v_new);
+  const int64_t rows = T * c.num_kv_heads;
+  const int64_t num_slots = (int64_t)c.num_blocks * 16;
+  if (c.head_dim == 128) {
+    dim3 grid((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)), 2);
+    hipLaunchKernelGGL(cache_write_kernel<128>, grid, dim3(kThreads), 0, s, k, v, slots, T, c.num_kv_heads,
+                       num_slots, err);
+  } else {
+    dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)), 2);
+    hipLaunchKernelGGL(cache_write_kernel<64>, grid, dim3(kThreads), 0, s, k, v, slots, T, c.num_kv_heads,
+                       num_slots, err);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(const CacheView& c, const uint16_t* k_src, const uint16_t* v_src, int first_block,
+                          int n_blocks, hipStream_t s) {
+  if (n_blocks == 0) return hipSuccess;
+  const RowSide k = side(c, true, k_src), v = side(c, false, v_src);
+  const int64_t rows = (int64_t)n_blocks * c.num_kv_heads * 16;
+  if (c.head_dim == 128) {
+    dim3 grid((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)), 2);
+    hipLaunchKernelGGL(convert_kernel<128>, grid, dim3(kThreads), 0, s, k, v, first_block, n_blocks,
+                       c.num_kv_heads);
+  } else {
+    dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)), 2);
+    hipLaunchKernelGGL(convert_kernel<64>, grid, dim3(kThreads), 0, s, k, v, first_block, n_blocks,
+                       c.num_kv_heads);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,202 @@
+// kvq_api.cpp — the C ABI of libkvq (declared in include/kvq.h): host-side
+// argument checks, launch geometry and dispatch to the HIP kernels.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state (and can be exercised without a GPU).
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kvq_launch.h"
+
+namespace {
+
+constexpr int kDefaultPartition = 512;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_store_dtype(int32_t d) {
+  return d == KVQ_BF16 || d == KVQ_INT8 || d == KVQ_FP8_E4M3 || d == KVQ_FP8_E5M2 || d == KVQ_INT4_ASYM;
+}
+
+// Checks shared by every call that takes a cache.
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_ERR_NULL;
+  if (!valid_store_dtype(c->k_dtype) || !valid_store_dtype(c->v_dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (c->block_size != 16) return KVQ_ERR_UNSUPPORTED;
+  if (c->num_kv_heads < 1 || c->num_blocks < 0) return KVQ_ERR_SHAPE;
+  if (!c->k_pages || !c->v_pages) return KVQ_ERR_NULL;
+  if (!aligned16(c->k_pages) || !aligned16(c->v_pages)) return KVQ_ERR_ALIGN;
+  const int32_t dts[2] = {c->k_dtype, c->v_dtype};
+  const int32_t grs[2] = {c->k_gran, c->v_gran};
+  const float* scales[2] = {c->k_scale, c->v_scale};
+  const float* metas[2] = {c->k_meta, c->v_meta};
+  for (int i = 0; i < 2; ++i) {
+    if (dts[i] == KVQ_INT4_ASYM) {
+      if (grs[i] != KVQ_PER_TOKEN_HEAD) return KVQ_ERR_UNSUPPORTED;
+      if (!metas[i]) return KVQ_ERR_NULL;
+      if (!aligned16(metas[i])) return KVQ_ERR_ALIGN;
+    } else if (dts[i] != KVQ_BF16) {
+      if (grs[i] != KVQ_PER_TENSOR && grs[i] != KVQ_PER_KV_HEAD) return KVQ_ERR_UNSUPPORTED;
+      (void)scales;  // NULL scale means 1.0
+    }
+  }
+  return KVQ_OK;
+}
+
+kvq::CacheView view(const kvq_cache* c) {
+  kvq::CacheView v;
+  v.k_dtype = c->k_dtype;
+  v.v_dtype = c->v_dtype;
+  v.k_gran = c->k_gran;
+  v.v_gran = c->v_gran;
+  v.num_blocks = c->num_blocks;
+  v.num_kv_heads = c->num_kv_heads;
+  v.head_dim = c->head_dim;
+  v.k_pages = static_cast<uint8_t*>(c->k_pages);
+  v.v_pages = static_cast<uint8_t*>(c->v_pages);
+  v.k_scale = c->k_dtype == KVQ_BF16 || c->k_dtype == KVQ_INT4_ASYM ? nullptr : c->k_scale;
+  v.v_scale = c->v_dtype == KVQ_BF16 || c->v_dtype == KVQ_INT4_ASYM ? nullptr : c->v_scale;
+  v.k_meta = c->k_meta;
+  v.v_meta = c->v_meta;
+  return v;
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+int effective_partition(int32_t partition) { return partition == 0 ? kDefaultPartition : partition; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_calibrate_scales(const uint16_t* x, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t granularity, int32_t target_dtype, float* absmax_inout, float* scale_out,
+                                void* stream) {
+  if (!absmax_inout || !scale_out) return KVQ_ERR_NULL;
+  if (num_tokens < 0 || num_kv_heads < 1) return KVQ_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (granularity != KVQ_PER_TENSOR && granularity != KVQ_PER_KV_HEAD) return KVQ_ERR_UNSUPPORTED;
+  float qmax;
+  switch (target_dtype) {
+    case KVQ_INT8: qmax = 127.0f; break;
+    case KVQ_FP8_E4M3: qmax = 448.0f; break;
+    case KVQ_FP8_E5M2: qmax = 57344.0f; break;
+    default: return KVQ_ERR_UNSUPPORTED;
+  }
+  if (num_tokens > 0) {
+    if (!x) return KVQ_ERR_NULL;
+    if (!aligned16(x)) return KVQ_ERR_ALIGN;
+    if (num_tokens > (int64_t)INT32_MAX * 256) return KVQ_ERR_SHAPE;
+  }
+  return from_hip(kvq::launch_calibrate(x, num_tokens, num_kv_heads, head_dim, granularity == KVQ_PER_KV_HEAD,
+                                        qmax, absmax_inout, scale_out, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_cache_write(const kvq_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens, int32_t* err_count, void* stream) {
+  const kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (num_tokens < 0) return KVQ_ERR_SHAPE;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k_new || !v_new || !slot_mapping) return KVQ_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGN;
+  const int64_t rows = num_tokens * cache->num_kv_heads;
+  const int64_t rows_per_block = 256 / (cache->head_dim / 8);
+  if ((rows + rows_per_block - 1) / rows_per_block > INT32_MAX) return KVQ_ERR_SHAPE;
+  return from_hip(kvq::launch_cache_write(view(cache), k_new, v_new, slot_mapping, num_tokens, err_count,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const uint16_t* v_src,
+                             int32_t first_block, int32_t num_blocks, void* stream) {
+  const kvq_status st = check_cache(dst);
+  if (st != KVQ_OK) return st;
+  if (first_block < 0 || num_blocks < 0 || (int64_t)first_block + num_blocks > dst->num_blocks) return KVQ_ERR_SHAPE;
+  if (num_blocks == 0) return KVQ_OK;
+  if (!k_src || !v_src) return KVQ_ERR_NULL;
+  if (!aligned16(k_src) || !aligned16(v_src)) return KVQ_ERR_ALIGN;
+  return from_hip(kvq::launch_convert(view(dst), k_src, v_src, first_block, num_blocks,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                                 int32_t partition) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition < 0) return 0;
+  const int part = effective_partition(partition);
+  const int64_t P = ((int64_t)max_seq_len + part - 1) / part;
+  if (P <= 1) return 0;
+  const int64_t rows = (int64_t)batch * num_q_heads;
+  // m and l: [rows][P] float each, rounded up to 16 bytes; acc: [rows][P][D]
+  const int64_t ml = ((rows * P * 4) + 15) / 16 * 16;
+  return (size_t)(2 * ml + rows * P * head_dim * 4);
+}
+
+kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                      int32_t max_seq_len, int32_t num_q_heads, float softmax_scale,
+                                      int32_t partition, void* workspace, size_t workspace_bytes,
+                                      int32_t out_dtype, void* out, int32_t* err_count, void* stream) {
+  const kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!kvq::decode_supported(cache->k_dtype, cache->v_dtype, cache->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (out_dtype != KVQ_BF16 && out_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
+  if (batch < 0 || max_seq_len < 0 || max_blocks_per_seq < 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads / cache->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  if (partition < 0 || partition % 16 != 0) return KVQ_ERR_SHAPE;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !block_tables || !seq_lens || !out) return KVQ_ERR_NULL;
+  if (!aligned16(q)) return KVQ_ERR_ALIGN;
+  if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_ERR_SHAPE;
+  const int part = effective_partition(partition);
+  const int64_t P64 = max_seq_len > 0 ? ((int64_t)max_seq_len + part - 1) / part : 1;
+  if (P64 > INT32_MAX) return KVQ_ERR_SHAPE;
+  const int P = (int)P64;
+  kvq::DecodeArgs a;
+  a.q = q;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.max_seq_len = max_seq_len;
+  a.num_q_heads = num_q_heads;
+  a.softmax_scale = softmax_scale;
+  a.partition = part;
+  a.num_partitions = P;
+  a.ws_m = a.ws_l = a.ws_o = nullptr;
+  if (P > 1) {
+    const size_t need = kvq_decode_workspace_size(batch, num_q_heads, cache->head_dim, max_seq_len, partition);
+    if (!workspace) return KVQ_ERR_WORKSPACE;
+    if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+    const int64_t rows = (int64_t)batch * num_q_heads;
+    const int64_t ml = ((rows * P * 4) + 15) / 16 * 16;
+    char* base = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(base);
+    a.ws_l = reinterpret_cast<float*>(base + ml);
+    a.ws_o = reinterpret_cast<float*>(base + 2 * ml);
+  }
+  a.out_f32 = out_dtype == KVQ_F32;
+  a.out = out;
+  a.err = err_count;
+  return from_hip(kvq::launch_decode(view(cache), a, static_cast<hipStream_t>(stream)));
+}
+
+const char* kvq_status_string(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_NULL: return "KVQ_ERR_NULL: a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "KVQ_ERR_SHAPE: a size is out of range or inconsistent";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: dtype, granularity or head_dim not supported";
+    case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: decode workspace missing or too small";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: a HIP launch failed";
+    default: return "unknown kvq_status";
+  }
+}
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+}  // extern "C"

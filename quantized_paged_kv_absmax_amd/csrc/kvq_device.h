@@ -1,0 +1,126 @@
+// kvq_device.h — device-side element codecs and small helpers for gfx950.
+//
+// Encode rules (quantise a float32 x with scale s; x / s is IEEE correctly
+// rounded — hipcc's default, never -ffast-math):
+//   INT8  q = clamp(RNE(x / s), -127, 127), NaN -> 0
+//         (the INT8 KV cache of the sm86 summary; RNE and the symmetric range
+//          are this library's reading)
+//   FP8   OCP e4m3 / e5m2 nearest value of x / s, ties to even, saturating to
+//         the largest finite value, NaN -> NaN code (the fp8_e4m3 / fp8_e5m2
+//         cache dtypes of vLLM PR 4893, description item 1)
+//   INT4  per row: s = (max - min) / 15, zp = RNE(-min / s), q = clamp(RNE(x / s)
+//         + zp, 0, 15) (vLLM issue 4025, methods item 1: scale + zero point)
+// Decode happens inside the attention kernel (decode.hip) as an exact conversion
+// of the codes to fp16 / bf16 MFMA operands, with the scales applied to the
+// float32 products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum : int { DT_BF16 = 0, DT_INT8 = 1, DT_E4M3 = 2, DT_E5M2 = 3, DT_INT4 = 4, DT_F32 = 5 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, round to nearest even (NaN -> quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// encoders
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t enc_int8(float x, float s) {
+  float t = x / s;
+  if (t != t) return 0u;
+  t = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)t & 0xffu;
+}
+
+template <int DT> struct Fp8Fmt;
+template <> struct Fp8Fmt<DT_E4M3> { static constexpr float kMax = 448.0f; static constexpr uint32_t kMaxCode = 0x7e; };
+template <> struct Fp8Fmt<DT_E5M2> { static constexpr float kMax = 57344.0f; static constexpr uint32_t kMaxCode = 0x7b; };
+
+// Nearest OCP fp8 code of a float32 t, ties to even, saturating (NaN -> 0x7f|sign).
+// Implemented on the float32 bit pattern: normal results drop the low mantissa
+// bits with round-to-nearest-even (a carry moves into the exponent), subnormal
+// results are RNE of t scaled by a power of two.
+template <int DT>
+__device__ __forceinline__ uint32_t enc_fp8_value(float t) {
+  constexpr int MB = (DT == DT_E4M3) ? 3 : 2;
+  constexpr int BIAS = (DT == DT_E4M3) ? 7 : 15;
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return sign | 0x7fu;            // NaN
+  const float a = fabsf(t);
+  if (a >= Fp8Fmt<DT>::kMax) return sign | Fp8Fmt<DT>::kMaxCode;       // saturate (incl. Inf)
+  const float min_normal = __uint_as_float((uint32_t)(127 + 1 - BIAS) << 23);
+  uint32_t mag;
+  if (a < min_normal) {
+    // subnormal fp8: value = n * 2^(1 - BIAS - MB); n = RNE(a / 2^(1 - BIAS - MB))
+    const float inv_q = __uint_as_float((uint32_t)(127 - (1 - BIAS - MB)) << 23);
+    mag = (uint32_t)rintf(a * inv_q);                                  // exact scaling
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    constexpr int SH = 23 - MB;
+    const uint32_t rem = ua & ((1u << SH) - 1u);
+    const uint32_t half = 1u << (SH - 1);
+    uint32_t qv = ua >> SH;
+    if (rem > half || (rem == half && (qv & 1u))) qv += 1u;
+    mag = qv - ((uint32_t)(127 - BIAS) << MB);                          // re-bias exponent
+  }
+  return sign | mag;
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t enc_fp8(float x, float s) { return enc_fp8_value<DT>(x / s); }
+
+// ---------------------------------------------------------------------------
+// byte permutes and fp16 magic-number conversions (exact)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// halves (1024 + b0, 1024 + b1) from bytes 0,1 (sel 0x04010400) or 2,3 (sel 0x04030402)
+// of x: the byte becomes the low mantissa byte of an fp16 with exponent 2^10.
+constexpr uint32_t kMagic64 = 0x64646464u;
+constexpr uint32_t kSelLo = 0x04010400u;
+constexpr uint32_t kSelHi = 0x04030402u;
+
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, f16x2 b) {
+  f16x2 v = __builtin_bit_cast(f16x2, a) + b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp8 e4m3 pair (bytes 0,1 or 2,3 of w) -> two fp16 (exact; NaN stays NaN)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// wave helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, 64); }
+
+}  // namespace kvq

@@ -1,0 +1,52 @@
+// kvq_launch.h — internal interface between the C ABI (kvq_api.cpp) and the
+// kernel launchers.  Everything here has already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct CacheView {
+  int k_dtype, v_dtype, k_gran, v_gran;
+  int num_blocks, num_kv_heads, head_dim;
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  const float* k_scale;
+  const float* v_scale;
+  float* k_meta;
+  float* v_meta;
+};
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t T, int Hkv, int D, int per_head, float qmax,
+                            float* absmax, float* scale, hipStream_t s);
+
+hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const uint16_t* v_new,
+                              const int64_t* slots, int64_t T, int32_t* err, hipStream_t s);
+
+hipError_t launch_convert(const CacheView& c, const uint16_t* k_src, const uint16_t* v_src,
+                          int first_block, int n_blocks, hipStream_t s);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int batch, max_seq_len, num_q_heads;
+  float softmax_scale;
+  int partition, num_partitions;
+  float* ws_m;   // [B][Hq][P]
+  float* ws_l;   // [B][Hq][P]
+  float* ws_o;   // [B][Hq][P][D]
+  int out_f32;
+  void* out;
+  int32_t* err;
+};
+
+// true if the (K dtype, V dtype, head_dim) combination has a kernel
+bool decode_supported(int k_dtype, int v_dtype, int head_dim);
+
+hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kvq

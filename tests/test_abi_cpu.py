@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports what include/kvq.h declares,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_paged_kv_absmax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libkvq.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvq_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(7):
+        assert lib.kvq_status_string(s).startswith(b"KVQ_")
+    assert lib.kvq_status_string(99) == b"unknown kvq_status"
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced on the host
+
+
+def _cache(**kw):
+    c = _lib.KvqCacheStruct()
+    c.k_dtype = c.v_dtype = _lib.INT8
+    c.k_gran = c.v_gran = _lib.PER_TENSOR
+    c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim = 8, 16, 2, 128
+    c.k_pages = c.v_pages = FAKE
+    c.k_scale = c.v_scale = None
+    c.k_meta = c.v_meta = None
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _decode(c, B=2, Hq=4, max_seq_len=100, partition=0, ws=None, ws_bytes=0, out_dtype=_lib.BF16, q=FAKE,
+            out=FAKE):
+    lib = _lib.load()
+    return lib.kvq_paged_attention_decode(ctypes.byref(c) if c is not None else None, q, FAKE, 8, FAKE, B,
+                                          max_seq_len, Hq, 0.088, partition, ws, ws_bytes, out_dtype, out, None,
+                                          None)
+
+
+def test_decode_argument_errors():
+    assert _decode(None) == _lib.ERR_NULL
+    assert _decode(_cache(head_dim=96)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(block_size=32)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(k_pages=None)) == _lib.ERR_NULL
+    assert _decode(_cache(v_pages=FAKE + 4)) == _lib.ERR_ALIGN
+    assert _decode(_cache(k_dtype=_lib.INT4_ASYM, k_gran=_lib.PER_TOKEN_HEAD, k_meta=FAKE)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(k_dtype=_lib.INT4_ASYM, k_gran=_lib.PER_TOKEN_HEAD)) == _lib.ERR_NULL
+    assert _decode(_cache(k_gran=_lib.PER_TOKEN_HEAD)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(k_dtype=9)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(), Hq=5) == _lib.ERR_SHAPE
+    assert _decode(_cache(), Hq=34) == _lib.ERR_UNSUPPORTED        # 17 query heads per KV head
+    assert _decode(_cache(), partition=24) == _lib.ERR_SHAPE
+    assert _decode(_cache(), out_dtype=_lib.INT8) == _lib.ERR_UNSUPPORTED
+    assert _decode(_cache(), q=FAKE + 2) == _lib.ERR_ALIGN
+    assert _decode(_cache(), out=None) == _lib.ERR_NULL
+    # a split decode needs a workspace of the advertised size
+    assert _decode(_cache(), max_seq_len=2000) == _lib.ERR_WORKSPACE
+    need = _lib.load().kvq_decode_workspace_size(2, 4, 128, 2000, 0)
+    assert _decode(_cache(), max_seq_len=2000, ws=FAKE, ws_bytes=need - 1) == _lib.ERR_WORKSPACE
+    assert _decode(_cache(), max_seq_len=2000, ws=FAKE + 8, ws_bytes=need) == _lib.ERR_ALIGN
+    # batch 0 is a no-op that succeeds without touching the device
+    assert _decode(_cache(), B=0) == _lib.OK
+
+
+def test_workspace_size():
+    lib = _lib.load()
+    assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 0) == 0            # one partition: none
+    assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 256) > 0
+    rows, P, D = 4 * 32, 3, 128                                              # 1100 tokens / 512
+    ml = (rows * P * 4 + 15) // 16 * 16
+    assert lib.kvq_decode_workspace_size(4, 32, 128, 1100, 0) == 2 * ml + rows * P * D * 4
+
+
+def test_write_convert_calibrate_argument_errors():
+    lib = _lib.load()
+    c = _cache()
+    assert lib.kvq_cache_write(None, FAKE, FAKE, FAKE, 4, None, None) == _lib.ERR_NULL
+    assert lib.kvq_cache_write(ctypes.byref(c), None, FAKE, FAKE, 4, None, None) == _lib.ERR_NULL
+    assert lib.kvq_cache_write(ctypes.byref(c), FAKE + 2, FAKE, FAKE, 4, None, None) == _lib.ERR_ALIGN
+    assert lib.kvq_cache_write(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None, None) == _lib.ERR_SHAPE
+    assert lib.kvq_cache_write(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None, None) == _lib.OK
+    assert lib.kvq_convert_cache(ctypes.byref(c), FAKE, FAKE, 4, 5, None) == _lib.ERR_SHAPE
+    assert lib.kvq_convert_cache(ctypes.byref(c), FAKE, FAKE, -1, 1, None) == _lib.ERR_SHAPE
+    assert lib.kvq_convert_cache(ctypes.byref(c), None, FAKE, 0, 1, None) == _lib.ERR_NULL
+    assert lib.kvq_convert_cache(ctypes.byref(c), FAKE, FAKE, 0, 0, None) == _lib.OK
+    assert lib.kvq_calibrate_scales(FAKE, 10, 2, 128, _lib.PER_TENSOR, _lib.INT8, None, FAKE, None) == _lib.ERR_NULL
+    assert lib.kvq_calibrate_scales(FAKE, 10, 2, 128, _lib.PER_TOKEN_HEAD, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_scales(FAKE, 10, 2, 128, _lib.PER_TENSOR, _lib.INT4_ASYM, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_scales(FAKE, 10, 2, 100, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_scales(None, 10, 2, 128, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_NULL
+    assert lib.kvq_calibrate_scales(FAKE + 4, 10, 2, 128, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_ALIGN

@@ -1,0 +1,142 @@
+"""GPU parity of the codecs, the cache write, the conversion and the calibration:
+bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_paged_kv_absmax_amd as kvq
+from oracle import cache as oc
+from oracle import codecs
+from tests.kvq_harness import dev_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def _write_rows(dtype, rows_bits, scale, gran="per_tensor", H=1):
+    """Write rows [T][H][D] at slots 0..T-1 of a fresh cache; return pages (numpy) and meta."""
+    T, H_, D = rows_bits.shape
+    nb = -(-T // 16)
+    c = kvq.PagedKVCache(nb, H_, D, dtype, dtype, k_gran=gran, v_gran=gran)
+    if scale is not None:
+        c.k_scale.copy_(torch.as_tensor(np.asarray(scale, np.float32).reshape(-1)))
+        c.v_scale.copy_(torch.as_tensor(np.asarray(scale, np.float32).reshape(-1)))
+    x = dev_bf16(rows_bits)
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    kvq.kvq_cache_write(c, x, x, slots)
+    torch.cuda.synchronize()
+    kp = c.k_pages.cpu().numpy().transpose(0, 2, 1, 3).reshape(nb * 16, H_, -1)[:T]
+    km = None if c.k_meta is None else c.k_meta.cpu().numpy().transpose(0, 2, 1, 3).reshape(nb * 16, H_, 2)[:T]
+    return kp, km
+
+
+@pytest.mark.parametrize("dtype", ["int8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 3.75e-3, 17.5, 2.0 ** -20])
+def test_encode_every_bf16_value(dtype, scale):
+    log(f"encode all bf16: {dtype} scale={scale}")
+    rows = ALL_BF16.reshape(512, 1, 128)
+    got, _ = _write_rows(dtype, rows, scale)
+    ref, _ = oc.encode_rows(rows, dtype, np.float32(scale))
+    if dtype == "int8":
+        assert np.array_equal(got, ref)
+    else:
+        nan = codecs.fp8_is_nan_code(ref, dtype)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert codecs.fp8_is_nan_code(got[nan], dtype).all()
+
+
+def test_encode_per_head_scales_d64():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((200, 4, 64)).astype(np.float32) * np.array([1, 10, 0.1, 300], np.float32)[None, :, None]
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    sc = np.array([0.01, 0.07, 0.0009, 2.5], np.float32)
+    for dtype in ("int8", "e4m3", "e5m2"):
+        got, _ = _write_rows(dtype, bits, sc, gran="per_kv_head")
+        ref, _ = oc.encode_rows(bits, dtype, sc)
+        assert np.array_equal(got, ref), dtype
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_int4_rows(D):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3000, 2, D)).astype(np.float32)
+    x[:, :, 5] *= 8
+    x[::9] = np.abs(x[::9]) + 2.0          # all-positive rows: zero point below 0
+    x[1::9] = -np.abs(x[1::9]) - 1.0       # all-negative rows
+    x[2::50] = 3.25                        # constant rows
+    x[3::50] = 0.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    got, gm = _write_rows("int4", bits, None)
+    ref, rm = oc.encode_rows(bits, "int4")
+    assert np.array_equal(got, ref)
+    assert np.array_equal(gm.view(np.uint32), rm.view(np.uint32))
+
+
+def test_bf16_copy_and_slot_errors():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 65536, size=(40, 2, 128)).astype(np.uint16)
+    c = kvq.PagedKVCache(4, 2, 128, "bf16", "bf16")
+    slots = np.arange(40, dtype=np.int64)
+    slots[3] = -1            # skipped silently
+    slots[7] = 4 * 16        # one past the pool: skipped and counted
+    slots[8] = 10 ** 12
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    x = dev_bf16(bits)
+    kvq.kvq_cache_write(c, x, x, torch.from_numpy(slots).cuda(), err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    pages = c.k_pages.cpu().numpy().view(np.uint16).reshape(4, 2, 16, 128).transpose(0, 2, 1, 3).reshape(64, 2, 128)
+    for i, s in enumerate(slots):
+        if 0 <= s < 64:
+            assert np.array_equal(pages[s], bits[i])
+    assert (pages[3] == 0xFFFF).all()      # never written
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_calibrate_bit_exact(D):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((1000, 8, D)).astype(np.float32) * rng.lognormal(0, 0.5, (1, 8, D)).astype(np.float32)
+    x[17, 3, 5] = -57.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    bits[100, 2, 7] = 0x7FC0           # a NaN is ignored
+    for gran, G in (("per_tensor", 1), ("per_kv_head", 8)):
+        for tgt in ("int8", "e4m3", "e5m2"):
+            a = torch.zeros(G, dtype=torch.float32, device="cuda")
+            s = torch.zeros(G, dtype=torch.float32, device="cuda")
+            # two batches accumulate into the running maximum
+            kvq.kvq_calibrate_scales(dev_bf16(bits[:333]), gran, tgt, a, s)
+            kvq.kvq_calibrate_scales(dev_bf16(bits[333:]), gran, tgt, a, s)
+            ra, rs = oc.calibrate(bits, gran, oc.QMAX[tgt])
+            assert np.array_equal(a.cpu().numpy(), ra), (gran, tgt)
+            assert np.array_equal(s.cpu().numpy(), rs), (gran, tgt)
+    # all zeros -> scale 1.0
+    a = torch.zeros(1, dtype=torch.float32, device="cuda")
+    s = torch.zeros(1, dtype=torch.float32, device="cuda")
+    kvq.kvq_calibrate_scales(dev_bf16(np.zeros((5, 2, D), np.uint16)), "per_tensor", "int8", a, s)
+    assert s.item() == 1.0 and a.item() == 0.0
+
+
+@pytest.mark.parametrize("dst", [("int4", "int4"), ("int8", "e4m3")])
+def test_convert_bit_exact(dst):
+    rng = np.random.default_rng(5)
+    nb, H, D = 37, 8, 128
+    x = rng.standard_normal((nb, H, 16, D)).astype(np.float32)
+    x[..., 9] *= 8
+    kb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    vb = ((x * 0.5).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    c = kvq.PagedKVCache(nb, H, D, dst[0], dst[1])
+    o = oc.PagedCache(nb, H, D, dst[0], dst[1], k_scale=np.float32(0.05) if dst[0] != "int4" else None,
+                      v_scale=np.float32(0.003) if dst[1] != "int4" else None)
+    if dst[0] != "int4":
+        c.k_scale.fill_(0.05)
+        c.v_scale.fill_(0.003)
+    kvq.kvq_convert_cache(c, dev_bf16(kb), dev_bf16(vb), 3, 30)
+    o.convert_from_bf16(kb, vb, 3, 30)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.k_pages.cpu().numpy(), o.k_pages)
+    assert np.array_equal(c.v_pages.cpu().numpy(), o.v_pages)
+    if dst[0] == "int4":
+        assert np.array_equal(c.k_meta.cpu().numpy().view(np.uint32), o.k_meta.view(np.uint32))
+        assert np.array_equal(c.v_meta.cpu().numpy().view(np.uint32), o.v_meta.view(np.uint32))

@@ -1,0 +1,161 @@
+"""GPU parity of the paged decode (and of the cache it reads) against the oracle,
+on every workload at reduced sizes that span several partitions and a ragged
+tail, plus the edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_paged_kv_absmax_amd as kvq
+from tests.kvq_harness import (assert_codes_equal, build_library_cache, build_oracle_cache, dev_bf16, gate_errors,
+                               library_decode, log, oracle_decode, softmax_scale)
+from workloads import WORKLOADS, make_decode_inputs
+from oracle import cache as oc
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_int8": {},
+    "llama8b_int8": dict(B=8, lens=("uniform", 20, 1500)),
+    "fp8_e4m3": dict(B=6),
+    "fp8_e4m3_s1": dict(B=6),
+    "fp8_e5m2": dict(B=6),
+    "fp8_hybrid": dict(B=6),
+    "longctx_int8": dict(B=2, lens=("uniform", 1000, 3000)),
+    "int4": dict(B=8, lens=("uniform", 20, 1500)),
+    "bf16": dict(B=6, lens=("uniform", 20, 1500)),
+}
+
+
+def _workload(name):
+    w = WORKLOADS[name]
+    if w.calib == "set":
+        w = w.with_(calib_set=(8, 512))
+    return w
+
+
+_cache = {}
+
+
+def _setup(name):
+    if name not in _cache:
+        w = _workload(name)
+        inp = make_decode_inputs(w, **CASES[name])
+        log(f"[{name}] B={inp.w.B} lens={inp.seq_lens.tolist()[:8]} blocks={inp.num_blocks}")
+        r = build_library_cache(w, inp)
+        o = build_oracle_cache(w, inp)
+        ref = oracle_decode(o, inp)
+        _cache.clear()
+        _cache[name] = (inp, r, o, ref)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_cache_codes_bit_exact(name):
+    inp, r, o, _ = _setup(name)
+    assert_codes_equal(r, o, inp)
+    assert int(r.err.item()) == 0
+    if o.kabs is not None:
+        assert np.array_equal(r.cache.k_absmax.cpu().numpy(), o.kabs)
+        assert np.array_equal(r.cache.k_scale.cpu().numpy(), o.k_scale)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("partition", [0, 64])
+def test_decode_within_tolerance(name, partition):
+    inp, r, o, ref = _setup(name)
+    for odt in ("f32", "bf16"):
+        out = library_decode(r, inp, partition=partition, out_dtype=odt)
+        torch.cuda.synchronize()
+        mx, nbad = gate_errors(out, ref, odt)
+        log(f"[{name}] partition={partition} out={odt} max|err|={mx:.3e} violations={nbad}")
+        assert nbad == 0
+
+
+@pytest.mark.parametrize("name", ["llama8b_int8", "fp8_hybrid", "int4"])
+def test_split_matches_unsplit_and_is_deterministic(name):
+    inp, r, o, ref = _setup(name)
+    a = library_decode(r, inp, partition=0, out_dtype="f32")
+    b = library_decode(r, inp, partition=0, out_dtype="f32")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)                                  # bit-identical reruns
+    # The PV product takes p in fp16, rounded relative to each partition's own
+    # running max: per weight a relative error of at most 2^-12, so two
+    # partitionings differ by at most 2 * 2^-12 * max|v_hat| (~1e-3 for the
+    # values here); both are separately within the oracle gate above.
+    vmax = float(np.abs(o.gather(inp.block_tables[0], int(inp.seq_lens[0]), "v")).max())
+    for part in (16, 128, 2048):
+        s = library_decode(r, inp, partition=part, out_dtype="f32")
+        torch.cuda.synchronize()
+        d = float((s - a).abs().max())
+        log(f"[{name}] split {part} vs unsplit: max|diff|={d:.3e} (bound {2 * 2 ** -12 * vmax:.3e})")
+        assert d <= 2 * 2 ** -12 * vmax, part
+
+
+def _small(Hq=8, Hkv=2, D=128, lens=(5, 16, 17, 0, 1, 512, 513), kd="int8", vd="int8"):
+    w = WORKLOADS["tiny_int8"].with_(Hq=Hq, Hkv=Hkv, D=D, k_dtype=kd, v_dtype=vd, B=len(lens),
+                                     lens=("fixed", tuple(lens)),
+                                     k_scale_mode="absmax" if kd in ("int8", "e4m3", "e5m2") else "one",
+                                     v_scale_mode="absmax" if vd in ("int8", "e4m3", "e5m2") else "one",
+                                     k_gran="per_token_head" if kd == "int4" else "per_tensor",
+                                     v_gran="per_token_head" if vd == "int4" else "per_tensor",
+                                     calib="all" if kd != "int4" else "none")
+    inp = make_decode_inputs(w)
+    return w, inp
+
+
+@pytest.mark.parametrize("kd,vd,D,Hq,Hkv", [
+    ("int8", "int8", 128, 8, 2), ("e5m2", "e4m3", 64, 16, 1), ("int4", "int4", 64, 6, 3),
+    ("bf16", "int8", 128, 32, 2), ("e4m3", "bf16", 64, 4, 4), ("int4", "int4", 128, 16, 1),
+])
+def test_edge_lengths_and_group_sizes(kd, vd, D, Hq, Hkv):
+    w, inp = _small(Hq=Hq, Hkv=Hkv, D=D, kd=kd, vd=vd)
+    r = build_library_cache(w, inp)
+    o = build_oracle_cache(w, inp)
+    assert_codes_equal(r, o, inp)
+    ref = oracle_decode(o, inp)
+    for part in (0, 16, 32):
+        out = library_decode(r, inp, partition=part, out_dtype="f32")
+        torch.cuda.synchronize()
+        mx, nbad = gate_errors(out, ref, "f32")
+        log(f"[edge {kd}/{vd} D={D} g={Hq // Hkv}] partition={part} max|err|={mx:.3e}")
+        assert nbad == 0
+        assert (out[3] == 0).all()                 # seq_len 0 -> zero row
+        assert torch.isfinite(out).all()           # NaN-coded unused slots never leak
+
+
+def test_bad_block_ids_are_counted_not_faulted():
+    w, inp = _small(lens=(40, 33))
+    r = build_library_cache(w, inp)
+    bt = r.bt.clone()
+    bt[0, 1] = -5
+    bt[1, 0] = 10 ** 6
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = kvq.kvq_paged_attention_decode(r.cache, r.q, bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                         out_dtype="f32", err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) >= 2
+    assert torch.isfinite(out[0]).all()
+
+
+def test_seq_len_clamped_to_max_and_counted():
+    w, inp = _small(lens=(40, 33))
+    r = build_library_cache(w, inp)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, 33, softmax_scale(w.D), out_dtype="f32",
+                                         err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    o = build_oracle_cache(w, inp)
+    from oracle import attention as oa
+    ref = oa.decode(o, inp.q_bits, inp.block_tables, np.minimum(inp.seq_lens, 33), softmax_scale(w.D))
+    mx, nbad = gate_errors(out, ref, "f32")
+    assert nbad == 0
+
+
+def test_empty_batch_is_a_noop():
+    c = kvq.PagedKVCache(2, 2, 128, "int8", "int8")
+    q = torch.zeros((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    out = kvq.kvq_paged_attention_decode(c, q, torch.zeros((0, 1), dtype=torch.int32, device="cuda"),
+                                         torch.zeros(0, dtype=torch.int32, device="cuda"), 0, 0.088)
+    assert out.shape == (0, 4, 128)
