@@ -1,0 +1,365 @@
+"""Benchmark of the quantized paged-KV decode path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--quick]
+
+Headline: the Llama-3-8B-shaped INT8 workload (64 sequences, lengths U[512,
+4096], 32 query / 8 KV heads, head dim 128, per-tensor absmax scales).  One step
+writes the new token of every sequence into the paged cache (kvq_cache_write)
+and runs the paged decode (kvq_paged_attention_decode, 512-token partitions,
+split-KV merge in the same launch).  The page pool is replicated R times
+(>= 1.5 GB in total) and step s uses copy s % R, so the 256 MB Infinity Cache
+cannot serve the pages from a previous step; inputs are resident in HBM before
+the timed region.
+
+value = algorithmic KV bytes read per step / step time (GB/s), where the KV bytes
+are sum_b L_b * Hkv * (K + V bytes per token-head: 2*D for 8-bit codes).
+The JSON line also carries the decode kernel's roofline, per-dtype decode
+figures for the other workloads, cache-write / convert / calibrate GB/s, and the
+oracle's CPU throughput on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_DEFEAT_BYTES = 1.5e9
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline only (no per-dtype lines)")
+    ap.add_argument("--only", default=None, help="comma list of per-dtype workloads to run")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch scale the
+    counters read on the decode kernel to bytes."""
+    import torch
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "dispatches": 5}))
+
+
+# bytes one (token, KV head) row of K or V occupies: codes, plus the float32
+# (scale, zero point) pair of INT4
+ROW_BYTES = {"bf16": lambda D: 2 * D, "int8": lambda D: D, "e4m3": lambda D: D, "e5m2": lambda D: D,
+             "int4": lambda D: D // 2 + 8}
+
+
+def kv_bytes(inp):
+    """Algorithmic KV bytes one decode reads: sum_b L_b * Hkv * (K row + V row)."""
+    w = inp.w
+    per = ROW_BYTES[w.k_dtype](w.D) + ROW_BYTES[w.v_dtype](w.D)
+    return int(inp.seq_lens.astype(np.int64).sum()) * w.Hkv * per
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "kvq_device.h"):
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, kernel_hash):
+    """HBM bytes per decode launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class GpuWorkload:
+    """A workload's cache on the GPU, replicated for rotation, plus its step inputs."""
+
+    def __init__(self, name, device, rotate=True):
+        import torch
+        import quantized_paged_kv_absmax_amd as kvq
+        from workloads import WORKLOADS, make_decode_inputs, make_calibration_set, scatter_rows_to_pages
+
+        self.torch, self.kvq = torch, kvq
+        w = WORKLOADS[name]
+        self.name, self.w = name, w
+        t0 = time.perf_counter()
+        inp = make_decode_inputs(w)
+        self.inp = inp
+        self.gen_s = time.perf_counter() - t0
+
+        def t16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+        c = kvq.PagedKVCache(inp.num_blocks, w.Hkv, w.D, w.k_dtype, w.v_dtype, k_gran=w.k_gran, v_gran=w.v_gran,
+                             device=device)
+        self.cache = c
+        self.extra = {}
+        qmax = {"int8": "int8", "e4m3": "e4m3", "e5m2": "e5m2"}
+        ck, cv = make_calibration_set(w, inp)
+        if w.k_scale_mode == "absmax" and w.k_dtype in qmax:
+            xk = t16(ck)
+            self.extra["calibrate_gbs"] = self._time_calibrate(xk, w.k_gran, w.k_dtype, c)
+            kvq.kvq_calibrate_scales(xk, w.k_gran, w.k_dtype, c.k_absmax, c.k_scale)
+            del xk
+        if w.v_scale_mode == "absmax" and w.v_dtype in qmax:
+            kvq.kvq_calibrate_scales(t16(cv), w.v_gran, w.v_dtype, c.v_absmax, c.v_scale)
+        mask = inp.prompt_mask()
+        new_idx = np.nonzero(~mask)[0]
+        if w.from_bf16_cache:
+            kp = t16(scatter_rows_to_pages(inp.k_bits, inp.slot_mapping, inp.num_blocks))
+            vp = t16(scatter_rows_to_pages(inp.v_bits, inp.slot_mapping, inp.num_blocks))
+            self.extra["convert"] = self._time_convert(kp, vp)
+            kvq.kvq_convert_cache(c, kp, vp)
+            del kp, vp
+        else:
+            pidx = np.nonzero(mask)[0]
+            kd, vd = t16(inp.k_bits[pidx]), t16(inp.v_bits[pidx])
+            sl = torch.from_numpy(inp.slot_mapping[pidx]).to(device)
+            self.extra["bulk_write"] = self._time_write(kd, vd, sl)
+            kvq.kvq_cache_write(c, kd, vd, sl)
+            del kd, vd, sl
+        # the decode step's own tokens (written inside the step)
+        self.k_new = t16(inp.k_bits[new_idx]) if new_idx.size else None
+        self.v_new = t16(inp.v_bits[new_idx]) if new_idx.size else None
+        self.slot_new = torch.from_numpy(inp.slot_mapping[new_idx]).to(device) if new_idx.size else None
+        if self.k_new is not None:
+            kvq.kvq_cache_write(c, self.k_new, self.v_new, self.slot_new)
+        torch.cuda.synchronize()
+        self.q = t16(inp.q_bits)
+        self.bt = torch.from_numpy(inp.block_tables).to(device)
+        self.sl = torch.from_numpy(inp.seq_lens).to(device)
+        self.sm = float(np.float32(1.0) / np.sqrt(np.float32(w.D)))
+        pool_bytes = c.k_pages.numel() + c.v_pages.numel() + (0 if c.k_meta is None else 8 * c.k_meta.numel())
+        self.R = max(2, int(np.ceil(MALL_DEFEAT_BYTES / pool_bytes))) if rotate else 1
+        self.copies = [(c.k_pages, c.v_pages, c.k_meta, c.v_meta)]
+        for _ in range(self.R - 1):
+            self.copies.append(tuple(None if t is None else t.clone() for t in self.copies[0]))
+        self.structs = []
+        for kp, vp, km, vm in self.copies:
+            s = c.struct(kp, vp)
+            if km is not None:
+                s.k_meta, s.v_meta = km.data_ptr(), vm.data_ptr()
+            self.structs.append(s)
+        ws = kvq.kvq_decode_workspace_size(w.B, w.Hq, w.D, inp.max_seq_len, w.partition)
+        self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
+        self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=device)
+        self.kv_bytes = kv_bytes(inp)
+        torch.cuda.synchronize()
+
+    # ---- pieces of the step ----
+    def write_new(self, i):
+        if self.k_new is not None:
+            self.kvq.kvq_cache_write(self.cache, self.k_new, self.v_new, self.slot_new, struct=self.structs[i % self.R])
+
+    def decode(self, i):
+        self.kvq.kvq_paged_attention_decode(self.cache, self.q, self.bt, self.sl, self.inp.max_seq_len, self.sm,
+                                            partition=self.w.partition, workspace=self.ws, out=self.out,
+                                            struct=self.structs[i % self.R])
+
+    # ---- timers for the set-up kernels (reported as extra figures) ----
+    def _events(self, fn, reps):
+        torch = self.torch
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    def _time_write(self, kd, vd, sl):
+        c, kvq = self.cache, self.kvq
+        scratch = kvq.PagedKVCache(c.num_blocks, c.num_kv_heads, c.head_dim, c.k_dtype, c.v_dtype,
+                                   k_gran=c.k_gran, v_gran=c.v_gran, device=kd.device)
+        t = self._events(lambda: kvq.kvq_cache_write(scratch, kd, vd, sl), 5)
+        T, H, D = kd.shape
+        rb = {0: 2 * D, 1: D, 2: D, 3: D, 4: D // 2 + 8}
+        moved = T * H * (2 * 2 * D) + T * H * (rb[c.k_dtype] + rb[c.v_dtype])
+        del scratch
+        return {"tokens": int(T), "us": t * 1e6, "gbs": moved / t / 1e9}
+
+    def _time_convert(self, kp, vp):
+        c, kvq = self.cache, self.kvq
+        t = self._events(lambda: kvq.kvq_convert_cache(c, kp, vp), 5)
+        n = kp.numel()
+        moved = 2 * n * 2 + 2 * (n // 2 + (n // c.head_dim) * 8)
+        return {"blocks": c.num_blocks, "us": t * 1e6, "gbs": moved / t / 1e9}
+
+    def _time_calibrate(self, x, gran, dt, c):
+        torch, kvq = self.torch, self.kvq
+        a = torch.zeros_like(c.k_absmax)
+        s = torch.zeros_like(c.k_scale)
+        t = self._events(lambda: kvq.kvq_calibrate_scales(x, gran, dt, a, s), 5)
+        return {"tokens": int(x.shape[0]), "us": t * 1e6, "gbs": x.numel() * 2 / t / 1e9}
+
+
+def time_steps(gw, steps, warmup, with_write=True):
+    """Warmup, then K timed steps bracketed by synchronize; per-step events around
+    the decode launch give the decode kernel's own average duration."""
+    torch = gw.torch
+    for i in range(warmup):
+        if with_write:
+            gw.write_new(i)
+        gw.decode(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        if with_write:
+            gw.write_new(i)
+        ev[i][0].record()
+        gw.decode(i)
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    dec = np.array([a.elapsed_time(b) for a, b in ev])
+    return total_ms / steps, dec
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle's decode on host cores over a bounded sample of the headline workload."""
+    import threadpoolctl
+    from oracle import attention as oa
+    from oracle import cache as oc
+    from workloads import WORKLOADS, make_decode_inputs, make_calibration_set
+
+    w = WORKLOADS["llama8b_int8"]
+    inp = make_decode_inputs(w)
+    ck, cv = make_calibration_set(w, inp)
+    _, ks = oc.calibrate(ck, "per_tensor", 127.0)
+    _, vs = oc.calibrate(cv, "per_tensor", 127.0)
+    cache = oc.PagedCache(inp.num_blocks, w.Hkv, w.D, "int8", "int8", k_scale=ks, v_scale=vs)
+    cache.write(inp.k_bits, inp.v_bits, inp.slot_mapping)
+    sm = float(np.float32(1.0) / np.sqrt(np.float32(w.D)))
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    while done < w.B and time.perf_counter() - t0 < budget_s:
+        oa.decode(cache, inp.q_bits, inp.block_tables, inp.seq_lens, sm, seqs=[done])
+        nbytes += int(inp.seq_lens[done]) * w.Hkv * 2 * w.D
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle fp64 decode of the first {done} of {w.B} sequences of the llama8b_int8 workload "
+                      f"({nbytes / 1e6:.1f} MB of int8 KV, {dt:.1f} s); host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    import torch
+    import quantized_paged_kv_absmax_amd as kvq
+    kvq.load()
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    gw = GpuWorkload("llama8b_int8", device)
+    print(f"[bench] llama8b_int8 ready: {gw.inp.seq_lens.sum()} tokens, KV {gw.kv_bytes / 1e6:.1f} MB, "
+          f"R={gw.R} rotating copies (gen {gw.gen_s:.1f}s)", file=sys.stderr, flush=True)
+    ms_step, dec = time_steps(gw, args.steps, args.warmup, with_write=True)
+    dec_ms = float(dec.mean())
+    value = gw.kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = gw.kv_bytes / (dec_ms * 1e-3) / 1e9
+    khash = decode_source_hash()
+    traffic = read_traffic("llama8b_int8", khash)
+    # write alone: the 1-token-per-sequence cache write of the step
+    wt = gw._events(lambda: gw.write_new(0), 50)
+    per_dtype = {"int8 (llama8b_int8)": {"decode_us": dec_ms * 1e3, "decode_gbs": achieved,
+                                         "frac_hbm": achieved / HBM_PEAK_GBS,
+                                         "decode_us_p10_p90": [float(np.percentile(dec, 10) * 1e3),
+                                                               float(np.percentile(dec, 90) * 1e3)]}}
+    extras = {"llama8b_int8": dict(gw.extra, step_write_us=wt * 1e6)}
+    del gw
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "bf16", "int4", "longctx_int8"]
+        if args.only:
+            names = [n for n in args.only.split(",") if n]
+        for name in names:
+            g2 = GpuWorkload(name, device)
+            steps = max(20, args.steps // (4 if name == "longctx_int8" else 1))
+            _, d2 = time_steps(g2, steps, 5, with_write=False)
+            t = float(d2.mean())
+            gbs = g2.kv_bytes / (t * 1e-3) / 1e9
+            per_dtype[f"{g2.w.k_dtype}/{g2.w.v_dtype} ({name})"] = {
+                "decode_us": t * 1e3, "decode_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "kv_mb": g2.kv_bytes / 1e6}
+            extras[name] = g2.extra
+            print(f"[bench] {name}: decode {t * 1e3:.1f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+            del g2
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    w = WORKLOADS_DESC
+    line = {
+        "metric": "paged-decode effective KV GB/s (% of 8 TB/s HBM) per KV dtype; cache-write GB/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": w,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_partition_kernel<INT8,INT8,128>", "kernel_source_hash": khash},
+        "cpu_baseline": cpu,
+        "per_dtype": per_dtype,
+        "extra": extras,
+    }
+    print(json.dumps(line))
+
+
+WORKLOADS_DESC = {
+    "workload": "llama8b_int8: single-layer decode step (write 1 new token per sequence + paged decode), "
+                "Llama-3-8B attention shape, INT8 KV with per-tensor absmax scales",
+    "batch": 64, "seq_len": "U[512,4096]", "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+    "block_size": 16, "partition": 512, "kv_dtype": "int8/int8",
+}
+
+if __name__ == "__main__":
+    main()

@@ -159,7 +159,10 @@ kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const 
 /*
  * kvq_decode_workspace_size — bytes of device workspace kvq_paged_attention_decode
  * needs for these sizes (0 when every sequence fits one partition).
- * partition = 0 selects the default (512 tokens).
+ * partition = 0 selects the default (512 tokens).  Layout, for reference:
+ * float32 max [batch][num_q_heads][P], sum [batch][num_q_heads][P] and
+ * accumulators [batch][num_q_heads][P][head_dim] (P = ceil(max_seq_len /
+ * partition)), each region 16-byte aligned.
  */
 size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition);
@@ -176,7 +179,8 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
  * Token position p of sequence b is read from page block_tables[b][p / 16],
  * offset p % 16.  Accumulation is float32.  Sequences are cut into partitions of
  * `partition` tokens (0 = 512); when max_seq_len exceeds it, per-partition
- * (max, sum, accumulator) go to the workspace and a reduce pass merges them.
+ * (max, sum, accumulator) go to the workspace and a second kernel merges them
+ * (split-KV reduce).
  *   q             (device) bf16 [batch][num_q_heads][head_dim]; |q| < 65504
  *   block_tables  (device) int32 [batch][max_blocks_per_seq]
  *   seq_lens      (device) int32 [batch]; <= 0 gives a zero output row; values
@@ -185,7 +189,9 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
  *   num_q_heads   multiple of num_kv_heads, at most 16 query heads per KV head
  *   partition     0 or a positive multiple of 16
  *   workspace     (device) >= kvq_decode_workspace_size(...) bytes, 16-B aligned;
- *                 may be NULL when that size is 0
+ *                 may be NULL when that size is 0; no initial contents needed.
+ *                 Calls that overlap in time (other streams) need workspaces of
+ *                 their own.
  *   out_dtype     KVQ_BF16 (round to nearest even) or KVQ_F32
  *   out           (device) [batch][num_q_heads][head_dim] of out_dtype
  * Supported K/V dtype pairs: any of {INT8, FP8_E4M3, FP8_E5M2, BF16} for K and for

@@ -2,11 +2,13 @@
 // methods item 3: read the stored codes, convert them to 16-bit, compute; vLLM
 // PR 4893: decode runs a paged-attention kernel), plus the split-KV reduce.
 //
-// Work unit: one workgroup per (partition, KV head, sequence) serves all g = Hq/Hkv
-// query heads of that KV head, so each K/V page is read from HBM exactly once.
-// NW waves split the partition's pages; each wave takes CH consecutive pages per
-// round and keeps its own online-softmax state, and the waves are merged through
-// LDS at the end.
+// Work unit: one wave (a 64-thread workgroup) per (partition, KV head, sequence)
+// serves all g = Hq/Hkv query heads of that KV head, so each K/V page is read from
+// HBM exactly once.  The wave streams its partition CH pages per round with an
+// online softmax; the K pages of round r+1 are loaded while round r's V pages are
+// consumed.  Each page is loaded through a buffer descriptor that spans exactly
+// that page (0 bytes for a page whose block id is out of range), so the loads
+// need no branches and an invalid page reads as zeros without touching memory.
 //
 // Per page (16 tokens) and wave:
 //   K: lane l loads token l%16, a quarter (l/16) of the row: D/4 elements.  The
@@ -29,6 +31,13 @@
 // Softmax runs in base 2 (log2 e folded into the logit scale).
 // Masking: positions >= seq_len get logit -inf and their V operand is zeroed
 // (an unused slot may hold a NaN code; 0 * NaN would leak).
+// Split KV: with more than one partition per sequence each wave writes (max, sum,
+// unnormalised output) of its partition to the workspace, and a second, small
+// kernel merges them (a kernel boundary instead of a device-wide fence: on this
+// chip an agent-scope release writes back the L2 of the issuing XCD, which costs
+// far more than the launch when thousands of waves do it).
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -37,7 +46,6 @@ namespace kvq {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kNW = 4;  // waves per workgroup
 
 struct Params {
   const uint8_t* k_pages;
@@ -56,9 +64,9 @@ struct Params {
   float sm_log2;  // softmax_scale * log2(e)
   int partition;
   int num_partitions;
-  float* ws_m;
-  float* ws_l;
-  float* ws_o;
+  float* ws_m;       // [B][Hq][P] running max (base 2) of each partition
+  float* ws_l;       // [B][Hq][P] softmax sum
+  float* ws_o;       // [B][Hq][P][D] unnormalised output
   int out_f32;
   void* out;
   int32_t* err;
@@ -69,10 +77,22 @@ struct Geo {
   static constexpr int kRowBytes = (DT == DT_BF16) ? 2 * D : (DT == DT_INT4) ? D / 2 : D;
   static constexpr int kKLaneBytes = kRowBytes / 4;   // K bytes per lane per page
   static constexpr int kKDw = kKLaneBytes / 4;        // ... in dwords
+  // A lane's K bytes are kNPC pieces of kPS bytes; piece j of lane group qg sits at
+  // row offset j*4*kPS + qg*kPS, so one load instruction reads, from each of the
+  // page's 16 rows, 4*kPS contiguous bytes (a whole 64-byte sector).
+  static constexpr int kPS = (kKLaneBytes < 16) ? kKLaneBytes : 16;
+  static constexpr int kNPC = kKLaneBytes / kPS;
   static constexpr int kNE = D / 16;                  // V columns per lane
   static constexpr int kVRowBytes = kRowBytes / 16;   // V bytes per lane per row
   static constexpr int kVDw = (kVRowBytes + 3) / 4;   // ... in dwords (int4 D=64: 2 bytes -> 1)
 };
+
+// row byte offset of dword dw of the K bytes of lane group qg
+template <int DT, int D>
+__device__ __forceinline__ int k_byte(int qg, int dw) {
+  constexpr int PS = Geo<DT, D>::kPS, DPP = PS / 4;
+  return (dw / DPP) * 4 * PS + qg * PS + 4 * (dw % DPP);
+}
 
 __device__ __forceinline__ int clamp_len(const Params& p, int b, bool count) {
   int L = p.seq_lens[b];
@@ -82,39 +102,6 @@ __device__ __forceinline__ int clamp_len(const Params& p, int b, bool count) {
     L = cap;
   }
   return L;
-}
-
-// ---------------------------------------------------------------------------
-// loads
-// ---------------------------------------------------------------------------
-
-template <int NDW>
-__device__ __forceinline__ void load_dw(uint32_t (&r)[NDW], const uint8_t* ptr) {
-  if constexpr (NDW % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < NDW / 4; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(ptr + 16 * i);
-      r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
-    }
-  } else if constexpr (NDW == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(ptr);
-    r[0] = v.x; r[1] = v.y;
-  } else {
-    static_assert(NDW == 1, "unsupported load width");
-    r[0] = *reinterpret_cast<const uint32_t*>(ptr);
-  }
-}
-
-// V bytes of one row for this lane: VRB bytes (2, 4, 8 or 16)
-template <int DT, int D, int N>
-__device__ __forceinline__ void load_v_row(uint32_t (&r)[N], const uint8_t* ptr) {
-  constexpr int VRB = Geo<DT, D>::kVRowBytes;
-  static_assert(N == Geo<DT, D>::kVDw, "V row width");
-  if constexpr (VRB == 2) {
-    r[0] = *reinterpret_cast<const uint16_t*>(ptr);
-  } else {
-    load_dw<N>(r, ptr);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -159,9 +146,30 @@ __device__ __forceinline__ u32x4 k_operand(const uint32_t (&kw)[N], int s) {
 // head-dim index of operand element e of k-step s for lane group qg (must match k_operand)
 template <int DT, int D>
 __device__ __forceinline__ int k_dim(int qg, int s, int e) {
-  const int base = (D / 4) * qg + 8 * s;
-  if constexpr (DT == DT_INT4) return base + ((e < 4) ? 2 * e : 2 * (e - 4) + 1);
-  return base + e;
+  if constexpr (DT == DT_INT4) return 2 * (k_byte<DT, D>(qg, s) + (e & 3)) + (e >> 2);
+  else if constexpr (DT == DT_BF16) return (k_byte<DT, D>(qg, 4 * s + (e >> 1)) + 2 * (e & 1)) >> 1;
+  else return k_byte<DT, D>(qg, 2 * s + (e >> 2)) + (e & 3);
+}
+
+// Integer path (INT8 and INT4 K): the K codes themselves are the operand of
+// v_mfma_i32_16x16x64_i8 (16 int8 values per lane and step).  INT4 codes are
+// split into even- and odd-element bytes (values 0..15).
+template <int DT, int D, int N>
+__device__ __forceinline__ u32x4 k_operand_i8(const uint32_t (&kw)[N], int s) {
+  static_assert(N == Geo<DT, D>::kKDw, "K lane width");
+  if constexpr (DT == DT_INT8) {
+    return u32x4{kw[4 * s], kw[4 * s + 1], kw[4 * s + 2], kw[4 * s + 3]};
+  } else {
+    const uint32_t w0 = kw[2 * s], w1 = kw[2 * s + 1];
+    return u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+  }
+}
+
+// head-dim index of element e (0..15) of integer-path step s (must match k_operand_i8)
+template <int DT, int D>
+__device__ __forceinline__ int k_dim_i8(int qg, int s, int e) {
+  if constexpr (DT == DT_INT8) return k_byte<DT, D>(qg, 4 * s + (e >> 2)) + (e & 3);
+  else return 2 * (k_byte<DT, D>(qg, 2 * s + (e >> 3)) + (e & 3)) + ((e >> 2) & 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,13 +208,13 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][N], u32x2 (&o
         uint32_t i0 = perm(vr[2 * pr + 1][j], vr[2 * pr][j], 0x05010400u);
         uint32_t i1 = perm(vr[2 * pr + 1][j], vr[2 * pr][j], 0x07030602u);
         if constexpr (DT == DT_INT8) {
-          const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+          // fp16 value 1152 + code; the 1152 offset is removed after the product
           i0 ^= 0x80808080u;
           i1 ^= 0x80808080u;
-          ob[4 * j + 0][pr] = pk_add_f16(perm(kMagic64, i0, kSelLo), bias);
-          ob[4 * j + 1][pr] = pk_add_f16(perm(kMagic64, i0, kSelHi), bias);
-          ob[4 * j + 2][pr] = pk_add_f16(perm(kMagic64, i1, kSelLo), bias);
-          ob[4 * j + 3][pr] = pk_add_f16(perm(kMagic64, i1, kSelHi), bias);
+          ob[4 * j + 0][pr] = perm(kMagic64, i0, kSelLo);
+          ob[4 * j + 1][pr] = perm(kMagic64, i0, kSelHi);
+          ob[4 * j + 2][pr] = perm(kMagic64, i1, kSelLo);
+          ob[4 * j + 3][pr] = perm(kMagic64, i1, kSelHi);
         } else {
           ob[4 * j + 0][pr] = e4m3x2_to_f16x2<false>(i0);
           ob[4 * j + 1][pr] = e4m3x2_to_f16x2<true>(i0);
@@ -215,8 +223,8 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][N], u32x2 (&o
         }
       }
     }
-  } else {  // INT4: byte k of a row holds columns 2k (low nibble), 2k+1 (high nibble)
-    const f16x2 bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  } else {  // INT4: byte k of a row holds columns 2k (low nibble), 2k+1 (high nibble);
+            // fp16 value 1024 + code, the offset removed after the product
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const uint32_t a = vr[2 * pr][0], b = vr[2 * pr + 1][0];
@@ -225,12 +233,12 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][N], u32x2 (&o
         const uint32_t la = hn ? ((a >> 4) & 0x0F0F0F0Fu) : (a & 0x0F0F0F0Fu);
         const uint32_t lb = hn ? ((b >> 4) & 0x0F0F0F0Fu) : (b & 0x0F0F0F0Fu);
         const uint32_t i0 = perm(lb, la, 0x05010400u);   // bytes 0,1 of both rows
-        ob[0 + hn][pr] = pk_add_f16(perm(kMagic64, i0, kSelLo), bias);   // column 2*0 + hn
-        ob[2 + hn][pr] = pk_add_f16(perm(kMagic64, i0, kSelHi), bias);   // column 2*1 + hn
+        ob[0 + hn][pr] = perm(kMagic64, i0, kSelLo);     // column 2*0 + hn
+        ob[2 + hn][pr] = perm(kMagic64, i0, kSelHi);     // column 2*1 + hn
         if constexpr (NE == 8) {
           const uint32_t i1 = perm(lb, la, 0x07030602u); // bytes 2,3
-          ob[4 + hn][pr] = pk_add_f16(perm(kMagic64, i1, kSelLo), bias);
-          ob[6 + hn][pr] = pk_add_f16(perm(kMagic64, i1, kSelHi), bias);
+          ob[4 + hn][pr] = perm(kMagic64, i1, kSelLo);
+          ob[6 + hn][pr] = perm(kMagic64, i1, kSelHi);
         }
       }
     }
@@ -261,6 +269,17 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, const f
                                                  0, 0);
 }
 
+__device__ __forceinline__ i32x4 mfma_i8(const u32x4& a, const u32x4& b, const i32x4& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
+                                               0);
+}
+
+// PV over two pages at once: k = 32 tokens
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma_pv2(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return mfma_qk<BF>(a, b, c);
+}
+
 __device__ __forceinline__ uint32_t pack2(float a, float b, bool bf) {
   if (bf) return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
   f16x2 v = {(_Float16)a, (_Float16)b};
@@ -277,31 +296,206 @@ __device__ __forceinline__ float unpack_hi(uint32_t v, bool bf) {
 }
 
 // ---------------------------------------------------------------------------
-// the partition kernel
+// per-page buffer resources: a page's K (or V, or INT4 metadata) rows form one
+// contiguous range; a descriptor covering exactly that range (0 bytes for an
+// invalid page) lets every lane load without a branch: out-of-range loads
+// return zeros and touch no memory.
 // ---------------------------------------------------------------------------
 
+constexpr int kRsrcFlags = 0x00020000;   // gfx9 buffer descriptor word 3 (raw 32-bit data)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
+}
+
+template <int NDW>
+__device__ __forceinline__ void buf_load(uint32_t (&r)[NDW], __amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (NDW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NDW / 4; ++i) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0));
+      r[4 * i] = v[0]; r[4 * i + 1] = v[1]; r[4 * i + 2] = v[2]; r[4 * i + 3] = v[3];
+    }
+  } else if constexpr (NDW == 2) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+    r[0] = v[0]; r[1] = v[1];
+  } else {
+    static_assert(NDW == 1, "unsupported load width");
+    r[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  }
+}
+
+// V bytes of one row for this lane: VRB bytes (2, 4, 8 or 16)
+template <int DT, int D, int N>
+__device__ __forceinline__ void buf_load_v_row(uint32_t (&r)[N], __amdgpu_buffer_rsrc_t rs, int off) {
+  static_assert(N == Geo<DT, D>::kVDw, "V row width");
+  if constexpr (Geo<DT, D>::kVRowBytes == 2) {
+    r[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+  } else {
+    buf_load<N>(r, rs, off);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV reduce: one workgroup per (query head, sequence) merges the
+// partitions:  o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j.
+// Lane groups of D/4 lanes (4 columns each) take every NG-th partition with a
+// running maximum, and LDS combines the groups.  A separate launch: the kernel
+// boundary makes every partition's stores visible without a device-wide fence.
+// ---------------------------------------------------------------------------
+
+constexpr int kRedThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
+  constexpr int LPG = D / 4;                  // lanes per group
+  constexpr int NG = kRedThreads / LPG;       // groups
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int L = clamp_len(p, b, false);
+  if (L <= 0) return;                         // the partition kernel wrote the zero row
+  const int P = (L + p.partition - 1) / p.partition;
+  const size_t row = (size_t)b * p.Hq + hq;
+  const float* m = p.ws_m + row * p.num_partitions;
+  const float* l = p.ws_l + row * p.num_partitions;
+  const float* o = p.ws_o + row * p.num_partitions * D;
+
+  const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = grp; j < P; j += NG) {
+    const float mj = m[j];
+    const float lj = l[j];
+    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * D + 4 * ln);
+    if (mj > M) {
+      const float sc = __builtin_amdgcn_exp2f(M - mj);
+      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+      den *= sc;
+      M = mj;
+    }
+    const float f = __builtin_amdgcn_exp2f(mj - M);
+    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    den += f * lj;
+  }
+  __shared__ float4 s_acc[NG][LPG];
+  __shared__ float s_m[NG], s_den[NG];
+  s_acc[grp][ln] = acc;
+  if (ln == 0) {
+    s_m[grp] = M;
+    s_den[grp] = den;
+  }
+  __syncthreads();
+  if (threadIdx.x < LPG) {
+    float MM = s_m[0];
+#pragma unroll
+    for (int gi = 1; gi < NG; ++gi) MM = fmaxf(MM, s_m[gi]);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dd = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float f = (s_m[gi] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[gi] - MM);
+      const float4 v = s_acc[gi][threadIdx.x];
+      a.x += f * v.x; a.y += f * v.y; a.z += f * v.z; a.w += f * v.w;
+      dd += f * s_den[gi];
+    }
+    const float r[4] = {a.x / dd, a.y / dd, a.z / dd, a.w / dd};
+    const size_t oi = row * D + 4 * threadIdx.x;
+    if (p.out_f32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(r[0]) | ((uint32_t)f32_to_bf16_bits(r[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(r[2]) | ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + oi) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the partition kernel: one wave per (partition, KV head, sequence)
+// ---------------------------------------------------------------------------
+
+// Block ids of the CH pages of one round (wave-uniform) and their validity.
+template <int CH>
+struct Round {
+  int bid[CH];
+  bool ok[CH];
+  int np;        // pages of this round inside the partition
+};
+
+// Block ids are fetched 64 pages at a time: lane i of a window register holds the
+// id of page 64*w + i of the partition (clamped to the last page), one window
+// ahead of its use, so reading an id is a v_readlane and never waits on memory.
+struct BlockIds {
+  const int32_t* bt;   // this sequence's block table, from the partition's first page
+  int n_pages;
+  int cur, nxt;        // window registers
+};
+
+__device__ __forceinline__ int load_window(const BlockIds& w, int win) {
+  const int pi = min(win * 64 + (int)threadIdx.x, w.n_pages - 1);
+  return w.bt[pi];
+}
+
+template <int CH>
+__device__ __forceinline__ Round<CH> fetch_round(const Params& p, BlockIds& ids, int first) {
+  static_assert(64 % CH == 0, "rounds never straddle a block-id window");
+  if (first > 0 && (first & 63) == 0) {       // entering the next window
+    ids.cur = ids.nxt;
+    ids.nxt = load_window(ids, (first >> 6) + 1);
+  }
+  Round<CH> r;
+  r.np = min(CH, ids.n_pages - first);
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int bb = __builtin_amdgcn_readlane(ids.cur, (first & 63) + i);
+    const bool inb = (bb >= 0) && (bb < p.num_blocks);
+    r.ok[i] = (i < r.np) && inb;
+    r.bid[i] = r.ok[i] ? bb : 0;
+    if (i < r.np && !inb) bad++;
+  }
+  if (bad && p.err && threadIdx.x == 0) atomicAdd(p.err, bad);
+  return r;
+}
+
+// lazy rescaling: the exponent reference of a head moves only when a logit exceeds
+// it by more than this (base 2), so p = 2^(z - m_ref) <= 256 stays finite in fp16
+// and the accumulators are rescaled only when a head's maximum jumps.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int KT, int VT, int D, int CH>
-__global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(Params p) {
+__global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
+  static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
   using KG = Geo<KT, D>;
   using VG = Geo<VT, D>;
   constexpr int NS = D / 32;       // QK k-steps
   constexpr int NE = VG::kNE;      // PV n-tiles
   constexpr bool KBF = (KT == DT_BF16);
   constexpr bool VBF = (VT == DT_BF16);
+  constexpr bool V_NAN = (VT == DT_E4M3 || VT == DT_E5M2 || VT == DT_BF16);  // codes that can decode to NaN/Inf
+  constexpr bool KI8 = (KT == DT_INT8 || KT == DT_INT4);   // integer QK path
+  constexpr int NSI = D / 64;                               // its k-steps (16 codes each)
+  // V operands carrying a constant offset (fp16 1152 + code, 1024 + code): the
+  // offset times sum_t p_t is removed after the product, with sum_t p_t taken from
+  // one more MFMA against a column of ones (the same rounded p the product saw)
+  constexpr bool V_FOLD = (VT == DT_INT8 || VT == DT_INT4);
+  constexpr float V_OFF = (VT == DT_INT8) ? 1152.0f : 1024.0f;
+  constexpr int KPAGE = 16 * KG::kRowBytes;   // bytes of one (block, head) K page
+  constexpr int VPAGE = 16 * VG::kRowBytes;
 
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int c = lane & 15, qg = lane >> 4;
   const int g = p.g;
 
-  const int L = clamp_len(p, b, part == 0 && kvh == 0 && threadIdx.x == 0);
+  // the length is the same for the whole wave: keep it (and all that derives
+  // from it: page counts, validity, buffer descriptors) in scalar registers
+  const int L = __builtin_amdgcn_readfirstlane(clamp_len(p, b, part == 0 && kvh == 0 && lane == 0));
   const int tok0 = part * p.partition;
   const bool single = (p.num_partitions == 1);
 
   if (L <= 0 || tok0 >= L) {
-    if (single && L <= 0) {
-      // zero output rows for this KV head's query heads
-      for (int i = threadIdx.x; i < g * D; i += kNW * 64) {
+    if (part == 0 && L <= 0) {
+      for (int i = lane; i < g * D; i += 64) {
         const size_t o = ((size_t)b * p.Hq + (size_t)kvh * g + i / D) * D + (i % D);
         if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = 0.0f;
         else reinterpret_cast<uint16_t*>(p.out)[o] = 0;
@@ -312,175 +506,202 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(Params p) {
   const int tok_end = min(L, tok0 + p.partition);
   const int n_pages = (tok_end - tok0 + 15) >> 4;
   const int pg0 = tok0 >> 4;
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
 
-  // ---- query operand: head c (zero if c >= g), k-dim order of the K operand ----
+  // ---- query operand: head c (zero if c >= g), in the k order of the K operand ----
   u32x4 qop[NS];
   float qsum = 0.0f;
-  {
+  // integer path: q = sq * (qh + ql / 256) with int8 qh, ql and a per-head scale
+  // sq = max|q| / 127 (a 16-bit fixed-point q; error <= 2^-8 sq per element)
+  u32x4 qhi[KI8 ? NSI : 1], qlo[KI8 ? NSI : 1];
+  float sq = 1.0f;
+  float qsum_i = 0.0f;   // INT4: 256 * sum(qh) + sum(ql) of head c
+  if constexpr (KI8) {
+    const bool hv = c < g;
+    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * g + (hv ? c : 0)) * D;
+    float qv[NSI][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < NSI; ++s2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        qv[s2][e] = hv ? bf16_bits_to_f32(qrow[k_dim_i8<KT, D>(qg, s2, e)]) : 0.0f;
+        amax = fmaxf(amax, fabsf(qv[s2][e]));
+      }
+    amax = fmaxf(amax, shfl_xor_f(amax, 16));
+    amax = fmaxf(amax, shfl_xor_f(amax, 32));
+    sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
+    const float inv = 1.0f / sq;
+    int sh = 0, sl = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < NSI; ++s2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t wh = 0, wl = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = qv[s2][4 * i + k] * inv;
+          const float h = fminf(fmaxf(rintf(x), -127.0f), 127.0f);
+          const float l = fminf(fmaxf(rintf((x - h) * 256.0f), -127.0f), 127.0f);
+          wh |= ((uint32_t)(int32_t)h & 0xffu) << (8 * k);
+          wl |= ((uint32_t)(int32_t)l & 0xffu) << (8 * k);
+          sh += (int)h;
+          sl += (int)l;
+        }
+        qhi[s2][i] = wh;
+        qlo[s2][i] = wl;
+      }
+    }
+    if constexpr (KT == DT_INT4) {
+      sh += __shfl_xor(sh, 16, 64);
+      sh += __shfl_xor(sh, 32, 64);
+      sl += __shfl_xor(sl, 16, 64);
+      sl += __shfl_xor(sl, 32, 64);
+      qsum_i = (float)(256 * sh + sl);
+    }
+  } else {
     const bool hv = c < g;
     const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * g + (hv ? c : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int base = (D / 4) * qg + 8 * s;
-      const uint4 raw = hv ? *reinterpret_cast<const uint4*>(qrow + base) : make_uint4(0, 0, 0, 0);
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-      float qf[8];
+      uint32_t qb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[e] = hv ? (uint32_t)qrow[k_dim<KT, D>(qg, s, e)] : 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qf[2 * i] = bf16_bits_to_f32(rw[i] & 0xffffu);
-        qf[2 * i + 1] = bf16_bits_to_f32(rw[i] >> 16);
-      }
-      float qe[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qe[e] = qf[k_dim<KT, D>(qg, s, e) - base];
-      if constexpr (KBF) {
-        qop[s] = u32x4{rw[0], rw[1], rw[2], rw[3]};
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(qe[2 * i], qe[2 * i + 1]));
+        if constexpr (KBF) {
+          qop[s][i] = qb[2 * i] | (qb[2 * i + 1] << 16);
+        } else {
+          f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(qb[2 * i]),
+                                                                          bf16_bits_to_f32(qb[2 * i + 1])));
           qop[s][i] = __builtin_bit_cast(uint32_t, h2);
-          if constexpr (KT == DT_INT4) qsum += (float)h2[0] + (float)h2[1];
         }
       }
     }
-    if constexpr (KT == DT_INT4) {
-      qsum += shfl_xor_f(qsum, 16);
-      qsum += shfl_xor_f(qsum, 32);
-    }
   }
 
-  // logit scale (base 2) for per-tensor / per-head K scales; INT4 scales per token
   float kfac = p.sm_log2;
   if constexpr (KT == DT_INT8 || KT == DT_E4M3 || KT == DT_E5M2) {
     if (p.k_scale) kfac *= p.k_scale[p.k_scale_per_head ? kvh : 0];
   }
+  // integer path: logit = kfac * sq / 256 * (256 acc_hi + acc_lo)
+  const float kq = kfac * sq * (1.0f / 256.0f);
+  const float kq4 = p.sm_log2 * sq * (1.0f / 256.0f);   // INT4: times the token's scale
 
   // ---- wave state ----
-  float m_run = -INFINITY;   // running max, head c (uniform over qg)
+  float m_ref = -INFINITY;   // exponent reference of head c (uniform over qg)
   float l_run = 0.0f;        // per-lane partial softmax sum
   float corr_run = 0.0f;     // INT4 V: per-lane partial of sum (p s) zp
   f32x4 oacc[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};   // V_FOLD: sum_t p_t per head (all columns alike)
 
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
-  const size_t head_stride = 16;  // rows per (block, head)
+  const size_t head_pages = (size_t)p.Hkv;                        // pages of one block: one per KV head
+  const int k_off = c * KG::kRowBytes + qg * KG::kPS;             // this lane's first K piece in a page
+  const int v_off = 4 * qg * VG::kRowBytes + c * VG::kVRowBytes;  // ... V bytes of its first row
+  const int meta_off = 4 * qg * 8;                                 // (s, zp) of tokens 4qg..4qg+3
 
-  for (int r0 = 0; r0 < n_pages; r0 += kNW * CH) {
-    const int wp0 = r0 + w * CH;
-    if (wp0 >= n_pages) continue;           // no pages for this wave this round
-    const int np = min(CH, n_pages - wp0);
-
-    int blk[CH];
-    bool pok[CH];
+  // ---- K loads of one round ----
+  uint32_t kw[CH][KG::kKDw];
+  float4 kmeta[CH][2];
+  auto load_k = [&](const Round<CH>& r) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      int bb = 0;
-      bool ok = false;
-      if (i < np) {
-        bb = bt[pg0 + wp0 + i];
-        ok = (bb >= 0) && (bb < p.num_blocks);
-        if (!ok) {
-          if (p.err && lane == 0) atomicAdd(p.err, 1);
-          bb = 0;
-        }
+      const size_t pidx = (size_t)r.bid[i] * head_pages + kvh;
+      const auto rs = page_rsrc(p.k_pages + pidx * KPAGE, r.ok[i] ? KPAGE : 0);
+#pragma unroll
+      for (int j = 0; j < KG::kNPC; ++j) {
+        uint32_t piece[KG::kPS / 4];
+        buf_load<KG::kPS / 4>(piece, rs, k_off + j * 4 * KG::kPS);
+#pragma unroll
+        for (int t = 0; t < KG::kPS / 4; ++t) kw[i][j * (KG::kPS / 4) + t] = piece[t];
       }
-      blk[i] = bb;
-      pok[i] = ok;
+      if constexpr (KT == DT_INT4) {
+        const auto rm = page_rsrc(p.k_meta + pidx * 32, r.ok[i] ? 128 : 0);
+        kmeta[i][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off, 0, 0));
+        kmeta[i][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off + 16, 0, 0));
+      }
     }
+  };
 
-    // ---- issue all loads of the round ----
-    uint32_t kw[CH][KG::kKDw];
+  // ---- one round: V loads, QK, (next K loads), softmax, PV ----
+  // TAIL: the partition's last round, the only one with pages past the end or a
+  // partial page; full rounds skip every per-token test.
+  auto round = [&](auto tail_tag, Round<CH>& cur, BlockIds& ids, int first) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
     uint32_t vw[CH][4][VG::kVDw];
-    float4 kmeta[CH][2], vmeta[CH][2];   // INT4: (s, zp) of tokens 4qg..4qg+3
-    // a page with a bad block id issues no load; its data stay zero and its
-    // tokens are masked below
+    float4 vmeta[CH][2];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      if (i < np) {
-        if (pok[i]) {
-          const size_t rowbase = ((size_t)blk[i] * p.Hkv + kvh) * head_stride;
-          load_dw<KG::kKDw>(kw[i], p.k_pages + (rowbase + c) * KG::kRowBytes + qg * KG::kKLaneBytes);
-          if constexpr (KT == DT_INT4) {
-            const float4* mp = reinterpret_cast<const float4*>(p.k_meta + (rowbase + 4 * qg) * 2);
-            kmeta[i][0] = mp[0];
-            kmeta[i][1] = mp[1];
-          }
-        } else {
+      const size_t pidx = (size_t)cur.bid[i] * head_pages + kvh;
+      const auto rs = page_rsrc(p.v_pages + pidx * VPAGE, cur.ok[i] ? VPAGE : 0);
 #pragma unroll
-          for (int k = 0; k < KG::kKDw; ++k) kw[i][k] = 0u;
-          kmeta[i][0] = kmeta[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+      for (int r = 0; r < 4; ++r) buf_load_v_row<VT, D>(vw[i][r], rs, v_off + r * VG::kRowBytes);
+      if constexpr (VT == DT_INT4) {
+        const auto rm = page_rsrc(p.v_meta + pidx * 32, cur.ok[i] ? 128 : 0);
+        vmeta[i][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off, 0, 0));
+        vmeta[i][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off + 16, 0, 0));
       }
     }
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < np) {
-        if (pok[i]) {
-          const size_t rowbase = ((size_t)blk[i] * p.Hkv + kvh) * head_stride;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            load_v_row<VT, D>(vw[i][r], p.v_pages + (rowbase + 4 * qg + r) * VG::kRowBytes + c * VG::kVRowBytes);
-          if constexpr (VT == DT_INT4) {
-            const float4* mp = reinterpret_cast<const float4*>(p.v_meta + (rowbase + 4 * qg) * 2);
-            vmeta[i][0] = mp[0];
-            vmeta[i][1] = mp[1];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int k = 0; k < VG::kVDw; ++k) vw[i][r][k] = 0u;
-          vmeta[i][0] = vmeta[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-    }
+    Round<CH> nxt;
+    if constexpr (!TAIL) nxt = fetch_round<CH>(p, ids, first + CH);
 
-    // ---- QK: logits of head c for tokens 4qg+r of each page ----
+    // QK: logits of head c for tokens 4qg+r of each page
     float sl[CH][4];
     float cmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      if (i < np) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KI8) {
+        i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc = mfma_qk<KBF>(k_operand<KT, D>(kw[i], s), qop[s], acc);
-        const int tbase = tok0 + (wp0 + i) * 16 + 4 * qg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float z;
-          if constexpr (KT == DT_INT4) {
-            const float ks = (r < 2) ? ((r == 0) ? kmeta[i][0].x : kmeta[i][0].z)
-                                     : ((r == 2) ? kmeta[i][1].x : kmeta[i][1].z);
-            const float kz = (r < 2) ? ((r == 0) ? kmeta[i][0].y : kmeta[i][0].w)
-                                     : ((r == 2) ? kmeta[i][1].y : kmeta[i][1].w);
-            z = (ks * p.sm_log2) * (acc[r] - kz * qsum);
-          } else {
-            z = acc[r] * kfac;
-          }
-          const bool valid = pok[i] && (tbase + r < tok_end);
-          z = valid ? z : -INFINITY;
-          sl[i][r] = z;
-          cmax = fmaxf(cmax, z);
+        for (int s2 = 0; s2 < NSI; ++s2) {
+          const u32x4 ko = k_operand_i8<KT, D>(kw[i], s2);
+          ah = mfma_i8(ko, qhi[s2], ah);
+          al = mfma_i8(ko, qlo[s2], al);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = (float)((ah[r] << 8) + al[r]);   // exact in int32
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sl[i][r] = -INFINITY;
+        for (int s2 = 0; s2 < NS; ++s2) acc = mfma_qk<KBF>(k_operand<KT, D>(kw[i], s2), qop[s2], acc);
+      }
+      const int tbase = tok0 + (first + i) * 16 + 4 * qg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float z;
+        if constexpr (KT == DT_INT4) {
+          const float ks = (r < 2) ? ((r == 0) ? kmeta[i][0].x : kmeta[i][0].z)
+                                   : ((r == 2) ? kmeta[i][1].x : kmeta[i][1].z);
+          const float kz = (r < 2) ? ((r == 0) ? kmeta[i][0].y : kmeta[i][0].w)
+                                   : ((r == 2) ? kmeta[i][1].y : kmeta[i][1].w);
+          z = (ks * kq4) * (acc[r] - kz * qsum_i);
+        } else if constexpr (KT == DT_INT8) {
+          z = acc[r] * kq;
+        } else {
+          z = acc[r] * kfac;
+        }
+        bool valid = cur.ok[i];
+        if constexpr (TAIL) valid = valid && (tbase + r < tok_end);
+        z = valid ? z : -INFINITY;
+        sl[i][r] = z;
+        cmax = fmaxf(cmax, z);
       }
     }
+
+    // K of the next round: the K registers are free now
+    if constexpr (!TAIL) load_k(nxt);
+
+    // lazy online-softmax update
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-
-    // ---- online softmax update ----
-    const float m_new = fmaxf(m_run, cmax);
-    const bool any = m_new != -INFINITY;
-    const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-    const float msub = any ? m_new : 0.0f;
-    m_run = m_new;
-    l_run *= alpha;
-    corr_run *= alpha;
-    {
+    const bool jump = cmax > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(jump)) {
+      const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - cmax) : 1.0f;   // m_ref = -inf -> 0
+      m_ref = jump ? cmax : m_ref;
+      l_run *= alpha;
+      corr_run *= alpha;
       float ar[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ar[r] = shfl_f(alpha, 4 * qg + r);   // alpha of head 4qg+r
@@ -488,62 +709,95 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(Params p) {
       for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[e][r] *= ar[r];
-    }
-
-    // ---- PV ----
+      if constexpr (V_FOLD) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < np) {
+        for (int r = 0; r < 4; ++r) sacc[r] *= ar[r];
+      }
+    }
+    const float msub = (m_ref == -INFINITY) ? 0.0f : m_ref;
+
+    // PV, two pages per MFMA (32 tokens)
+#pragma unroll
+    for (int i = 0; i < CH; i += 2) {
+      u32x4 aop;
+      u32x4 aop_lo;   // BF16 V: p = p_hi + p_lo, both bf16 (p_hi alone carries only 8 bits)
+      u32x2 vop[2][NE];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pi = i + h2;
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(sl[i][r] - msub);     // -inf -> 0
+          pr[r] = __builtin_amdgcn_exp2f(sl[pi][r] - msub);     // -inf -> 0
           l_run += pr[r];
         }
-        u32x2 aop;
+        uint32_t a0, a1;
         if constexpr (VT == DT_INT4) {
-          const float vs[4] = {vmeta[i][0].x, vmeta[i][0].z, vmeta[i][1].x, vmeta[i][1].z};
-          const float vz[4] = {vmeta[i][0].y, vmeta[i][0].w, vmeta[i][1].y, vmeta[i][1].w};
+          const float vs[4] = {vmeta[pi][0].x, vmeta[pi][0].z, vmeta[pi][1].x, vmeta[pi][1].z};
+          const float vz[4] = {vmeta[pi][0].y, vmeta[pi][0].w, vmeta[pi][1].y, vmeta[pi][1].w};
           float ps[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ps[r] = (pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
-          aop[0] = pack2(ps[0], ps[1], false);
-          aop[1] = pack2(ps[2], ps[3], false);
-          // correction uses the rounded operand values the MFMA sees
-          const float r0 = unpack_lo(aop[0], false), r1 = unpack_hi(aop[0], false);
-          const float r2 = unpack_lo(aop[1], false), r3 = unpack_hi(aop[1], false);
+          a0 = pack2(ps[0], ps[1], false);
+          a1 = pack2(ps[2], ps[3], false);
+          // the correction uses the rounded operand values the MFMA sees
+          const float r0 = unpack_lo(a0, false), r1 = unpack_hi(a0, false);
+          const float r2 = unpack_lo(a1, false), r3 = unpack_hi(a1, false);
           corr_run += (r0 != 0.f ? r0 * vz[0] : 0.f) + (r1 != 0.f ? r1 * vz[1] : 0.f) +
                       (r2 != 0.f ? r2 * vz[2] : 0.f) + (r3 != 0.f ? r3 * vz[3] : 0.f);
         } else {
-          aop[0] = pack2(pr[0], pr[1], VBF);
-          aop[1] = pack2(pr[2], pr[3], VBF);
+          a0 = pack2(pr[0], pr[1], VBF);
+          a1 = pack2(pr[2], pr[3], VBF);
         }
-        if (c >= g) aop = u32x2{0u, 0u};
+        aop[2 * h2] = (c < g) ? a0 : 0u;
+        aop[2 * h2 + 1] = (c < g) ? a1 : 0u;
+        if constexpr (VBF) {
+          const uint32_t l0 = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
+          const uint32_t l1 = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
+          aop_lo[2 * h2] = (c < g) ? l0 : 0u;
+          aop_lo[2 * h2 + 1] = (c < g) ? l1 : 0u;
+        }
 
-        u32x2 vop[NE];
-        v_operands<VT, D>(vw[i], vop);
-        // zero V operands of tokens that are not valid (tail of the last page, bad block)
-        const int tbase = tok0 + (wp0 + i) * 16 + 4 * qg;
-        const bool full = pok[i] && (tok0 + (wp0 + i) * 16 + 16 <= tok_end);
-        if (!full) {
-          uint32_t m01 = 0, m23 = 0;
-          if (pok[i]) {
-            m01 = ((tbase + 0 < tok_end) ? 0x0000ffffu : 0u) | ((tbase + 1 < tok_end) ? 0xffff0000u : 0u);
-            m23 = ((tbase + 2 < tok_end) ? 0x0000ffffu : 0u) | ((tbase + 3 < tok_end) ? 0xffff0000u : 0u);
-          }
+        v_operands<VT, D>(vw[pi], vop[h2]);
+        if constexpr (TAIL && V_NAN) {
+          // tokens past the end of the sequence: their slots may hold NaN codes
+          const int tb = tok0 + (first + pi) * 16 + 4 * qg;
+          const uint32_t m01 = ((tb + 0 < tok_end) ? 0x0000ffffu : 0u) | ((tb + 1 < tok_end) ? 0xffff0000u : 0u);
+          const uint32_t m23 = ((tb + 2 < tok_end) ? 0x0000ffffu : 0u) | ((tb + 3 < tok_end) ? 0xffff0000u : 0u);
 #pragma unroll
           for (int e = 0; e < NE; ++e) {
-            vop[e][0] &= m01;
-            vop[e][1] &= m23;
+            vop[h2][e][0] &= m01;
+            vop[h2][e][1] &= m23;
           }
         }
+      }
 #pragma unroll
-        for (int e = 0; e < NE; ++e) oacc[e] = mfma_pv<VBF>(aop, vop[e], oacc[e]);
+      for (int e = 0; e < NE; ++e) {
+        const u32x4 bop = {vop[0][e][0], vop[0][e][1], vop[1][e][0], vop[1][e][1]};
+        oacc[e] = mfma_pv2<VBF>(aop, bop, oacc[e]);
+        if constexpr (VBF) oacc[e] = mfma_pv2<VBF>(aop_lo, bop, oacc[e]);
+      }
+      if constexpr (V_FOLD) {
+        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
+        sacc = mfma_pv2<false>(aop, ones, sacc);
       }
     }
-  }
+    if constexpr (!TAIL) cur = nxt;
+  };
 
-  // ---- finish the wave: full sums over the lane groups ----
+  // ---- prologue: block ids and K of the first round; then the rounds ----
+  BlockIds ids;
+  ids.bt = bt + pg0;
+  ids.n_pages = n_pages;
+  ids.cur = load_window(ids, 0);
+  ids.nxt = load_window(ids, 1);
+  Round<CH> cur = fetch_round<CH>(p, ids, 0);
+  load_k(cur);
+  const int n_rounds = (n_pages + CH - 1) / CH;
+  for (int rr = 0; rr + 1 < n_rounds; ++rr) round(std::false_type{}, cur, ids, rr * CH);
+  round(std::true_type{}, cur, ids, (n_rounds - 1) * CH);
+
+  // ---- full softmax sums over the lane groups ----
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
   if constexpr (VT == DT_INT4) {
@@ -551,132 +805,54 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(Params p) {
     corr_run += shfl_xor_f(corr_run, 32);
   }
 
-  // ---- merge the waves through LDS ----
-  __shared__ float s_m[kNW][16], s_l[kNW][16], s_c[kNW][16];
-  __shared__ float s_o[kNW][16][D];
-  if (qg == 0) {
-    s_m[w][c] = m_run;
-    s_l[w][c] = l_run;
-    s_c[w][c] = corr_run;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * qg + r;
-    if (h < g) {
-      float M = s_m[0][h];
-#pragma unroll
-      for (int ww = 1; ww < kNW; ++ww) M = fmaxf(M, s_m[ww][h]);
-      const float mw = s_m[w][h];
-      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-#pragma unroll
-      for (int e = 0; e < NE; ++e) s_o[w][h][NE * c + e] = f * oacc[e][r];
-    }
-  }
-  __syncthreads();
-
   float vfac = 1.0f;
   if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
     if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
   }
-  for (int i = threadIdx.x; i < g * D; i += kNW * 64) {
-    const int h = i / D, d = i % D;
-    float M = s_m[0][h];
+
+  // lane (qg, c) holds O[head 4qg+r][d = NE*c + e]; fetch that head's sums
+  float lh[4], ch[4], mh[4];
 #pragma unroll
-    for (int ww = 1; ww < kNW; ++ww) M = fmaxf(M, s_m[ww][h]);
-    float num = 0.f, den = 0.f, cor = 0.f;
+  for (int r = 0; r < 4; ++r) {
+    lh[r] = shfl_f(l_run, 4 * qg + r);
+    ch[r] = shfl_f(corr_run, 4 * qg + r);
+    mh[r] = shfl_f(m_ref, 4 * qg + r);
+  }
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) {
-      const float mw = s_m[ww][h];
-      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-      num += s_o[ww][h][d];
-      den += f * s_l[ww][h];
-      if constexpr (VT == DT_INT4) cor += f * s_c[ww][h];
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * qg + r;
+    if (h >= g) continue;
+    const size_t row = (size_t)b * p.Hq + (size_t)kvh * g + h;
+    float o[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float v = oacc[e][r] - ch[r];
+      if constexpr (V_FOLD) v -= V_OFF * sacc[r];
+      o[e] = v * vfac;
     }
-    num = (num - cor) * vfac;
-    const int hq = kvh * g + h;
     if (single) {
-      const float o = num / den;
-      const size_t oi = ((size_t)b * p.Hq + hq) * D + d;
-      if (p.out_f32) reinterpret_cast<float*>(p.out)[oi] = o;
-      else reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_bits(o);
-    } else {
-      const size_t row = (size_t)b * p.Hq + hq;
-      p.ws_o[(row * p.num_partitions + part) * D + d] = num;
-      if (d == 0) {
-        p.ws_m[row * p.num_partitions + part] = M;
-        p.ws_l[row * p.num_partitions + part] = den;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] = o[e] / lh[r];
+      if (p.out_f32) {
+        float* dst = reinterpret_cast<float*>(p.out) + row * D + NE * c;
+#pragma unroll
+        for (int e = 0; e < NE; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + NE * c;
+        uint32_t pk[NE / 2];
+#pragma unroll
+        for (int e = 0; e < NE; e += 2) pk[e / 2] = (uint32_t)f32_to_bf16_bits(o[e]) | ((uint32_t)f32_to_bf16_bits(o[e + 1]) << 16);
+        if constexpr (NE == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
       }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// split-KV reduce: o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j
-// ---------------------------------------------------------------------------
-
-constexpr int kRedThreads = 256;
-
-template <int D>
-__global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
-  constexpr int LPG = D / 4;                  // lanes per group, 4 columns each
-  constexpr int NG = kRedThreads / LPG;       // groups
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int L = clamp_len(p, b, false);
-  const size_t orow = ((size_t)b * p.Hq + hq) * D;
-  if (L <= 0) {
-    for (int d = threadIdx.x; d < D; d += kRedThreads) {
-      if (p.out_f32) reinterpret_cast<float*>(p.out)[orow + d] = 0.0f;
-      else reinterpret_cast<uint16_t*>(p.out)[orow + d] = 0;
-    }
-    return;
-  }
-  const int P = (L + p.partition - 1) / p.partition;
-  const size_t row = (size_t)b * p.Hq + hq;
-  const float* m = p.ws_m + row * p.num_partitions;
-  const float* l = p.ws_l + row * p.num_partitions;
-  const float* o = p.ws_o + row * p.num_partitions * D;
-
-  __shared__ float s_red[kRedThreads / 64];
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < P; j += kRedThreads) mx = fmaxf(mx, m[j]);
+    } else {
+      float* dst = p.ws_o + (row * p.num_partitions + part) * D + NE * c;
 #pragma unroll
-  for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 64));
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  float M = s_red[0];
-#pragma unroll
-  for (int i = 1; i < kRedThreads / 64; ++i) M = fmaxf(M, s_red[i]);
-
-  const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  for (int j = grp; j < P; j += NG) {
-    const float f = __builtin_amdgcn_exp2f(m[j] - M);
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * D + 4 * ln);
-    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
-    den += f * l[j];
-  }
-  __shared__ float4 s_acc[NG][LPG];
-  __shared__ float s_den[NG];
-  s_acc[grp][ln] = acc;
-  if (ln == 0) s_den[grp] = den;
-  __syncthreads();
-  if (threadIdx.x < LPG) {
-    float4 a = s_acc[0][threadIdx.x];
-    float dd = s_den[0];
-#pragma unroll
-    for (int gi = 1; gi < NG; ++gi) {
-      const float4 v = s_acc[gi][threadIdx.x];
-      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-      dd += s_den[gi];
-    }
-    const float r[4] = {a.x / dd, a.y / dd, a.z / dd, a.w / dd};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const size_t oi = orow + 4 * threadIdx.x + k;
-      if (p.out_f32) reinterpret_cast<float*>(p.out)[oi] = r[k];
-      else reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_bits(r[k]);
+      for (int e = 0; e < NE; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+      if (c == 0) {
+        p.ws_m[row * p.num_partitions + part] = mh[r];
+        p.ws_l[row * p.num_partitions + part] = lh[r];
+      }
     }
   }
 }
@@ -685,15 +861,15 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
 // dispatch
 // ---------------------------------------------------------------------------
 
+// pages a wave streams per round (K of the next round is in flight meanwhile)
 template <int KT, int VT>
 constexpr int pages_per_round() {
-  return (KT == DT_BF16 || VT == DT_BF16 || KT == DT_INT4 || VT == DT_INT4) ? 4 : 8;
+  return (KT == DT_BF16 || VT == DT_BF16) ? 2 : 4;
 }
 
 template <int KT, int VT, int D>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, D, pages_per_round<KT, VT>()>), grid, dim3(kNW * 64), 0, s,
-                     prm);
+  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, D, pages_per_round<KT, VT>()>), grid, dim3(64), 0, s, prm);
   return hipGetLastError();
 }
 

@@ -67,6 +67,24 @@ kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HI
 
 int effective_partition(int32_t partition) { return partition == 0 ? kDefaultPartition : partition; }
 
+// Decode workspace: [m f32 [B][Hq][P]] [l f32 [B][Hq][P]] [acc f32 [B][Hq][P][D]],
+// each region starting on a 16-byte boundary.
+struct WsLayout {
+  int64_t m, l, o, total;
+};
+
+int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
+
+WsLayout workspace_layout(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t P) {
+  WsLayout w;
+  const int64_t rows = batch * num_q_heads;
+  w.m = 0;
+  w.l = w.m + round16(rows * P * 4);
+  w.o = w.l + round16(rows * P * 4);
+  w.total = w.o + rows * P * head_dim * 4;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,10 +145,7 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
   const int part = effective_partition(partition);
   const int64_t P = ((int64_t)max_seq_len + part - 1) / part;
   if (P <= 1) return 0;
-  const int64_t rows = (int64_t)batch * num_q_heads;
-  // m and l: [rows][P] float each, rounded up to 16 bytes; acc: [rows][P][D]
-  const int64_t ml = ((rows * P * 4) + 15) / 16 * 16;
-  return (size_t)(2 * ml + rows * P * head_dim * 4);
+  return workspace_layout(batch, num_q_heads, head_dim, P).total;
 }
 
 kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q, const int32_t* block_tables,
@@ -171,12 +186,11 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
     if (!workspace) return KVQ_ERR_WORKSPACE;
     if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
-    const int64_t rows = (int64_t)batch * num_q_heads;
-    const int64_t ml = ((rows * P * 4) + 15) / 16 * 16;
+    const WsLayout lay = workspace_layout(batch, num_q_heads, cache->head_dim, P);
     char* base = static_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(base);
-    a.ws_l = reinterpret_cast<float*>(base + ml);
-    a.ws_o = reinterpret_cast<float*>(base + 2 * ml);
+    a.ws_m = reinterpret_cast<float*>(base + lay.m);
+    a.ws_l = reinterpret_cast<float*>(base + lay.l);
+    a.ws_o = reinterpret_cast<float*>(base + lay.o);
   }
   a.out_f32 = out_dtype == KVQ_F32;
   a.out = out;

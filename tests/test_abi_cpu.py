@@ -91,8 +91,8 @@ def test_workspace_size():
     assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 0) == 0            # one partition: none
     assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 256) > 0
     rows, P, D = 4 * 32, 3, 128                                              # 1100 tokens / 512
-    ml = (rows * P * 4 + 15) // 16 * 16
-    assert lib.kvq_decode_workspace_size(4, 32, 128, 1100, 0) == 2 * ml + rows * P * D * 4
+    r16 = lambda x: (x + 15) // 16 * 16
+    assert lib.kvq_decode_workspace_size(4, 32, 128, 1100, 0) == 2 * r16(rows * P * 4) + rows * P * D * 4
 
 
 def test_write_convert_calibrate_argument_errors():
