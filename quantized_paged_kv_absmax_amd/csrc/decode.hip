@@ -419,6 +419,7 @@ struct Round {
   int bid[CH];
   bool ok[CH];
   int np;        // pages of this round inside the partition
+  int nbad;      // of those, pages with an out-of-range block id
 };
 
 // Block ids are fetched 64 pages at a time: lane i of a window register holds the
@@ -436,7 +437,7 @@ __device__ __forceinline__ int load_window(const BlockIds& w, int win) {
 }
 
 template <int CH>
-__device__ __forceinline__ Round<CH> fetch_round(const Params& p, BlockIds& ids, int first) {
+__device__ __forceinline__ Round<CH> fetch_round_nocount(const Params& p, BlockIds& ids, int first) {
   static_assert(64 % CH == 0, "rounds never straddle a block-id window");
   if (first > 0 && (first & 63) == 0) {       // entering the next window
     ids.cur = ids.nxt;
@@ -444,17 +445,109 @@ __device__ __forceinline__ Round<CH> fetch_round(const Params& p, BlockIds& ids,
   }
   Round<CH> r;
   r.np = min(CH, ids.n_pages - first);
-  int bad = 0;
+  r.nbad = 0;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int bb = __builtin_amdgcn_readlane(ids.cur, (first & 63) + i);
     const bool inb = (bb >= 0) && (bb < p.num_blocks);
     r.ok[i] = (i < r.np) && inb;
     r.bid[i] = r.ok[i] ? bb : 0;
-    if (i < r.np && !inb) bad++;
+    if (i < r.np && !inb) r.nbad++;
   }
-  if (bad && p.err && threadIdx.x == 0) atomicAdd(p.err, bad);
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging.  A wave streams its partition through an NST-deep ring of LDS
+// stages; a stage holds the K and V pages (and INT4 metadata) of one round of CH
+// pages.  Pages arrive by buffer_load ... lds DMA: each instruction moves 1 KB
+// (64 lanes x 16 B) of one page, whole 128-byte lines, without passing through
+// VGPRs, so the ring can hold several rounds in flight.  The 16-byte chunks of a
+// row are XOR-swizzled by the row index, which the per-lane source offsets of the
+// DMA apply and the ds_read addresses undo; the MFMA-layout reads (16 rows, same
+// column) then hit distinct banks.
+// ---------------------------------------------------------------------------
+
+template <int DT, int D>
+struct LdsPage {
+  static constexpr int RB = Geo<DT, D>::kRowBytes;
+  static constexpr int CPR = RB / 16;                         // 16-byte chunks per row
+  static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
+  static constexpr int PAGE = 16 * RB;
+  static constexpr int SLOT = PAGE < 1024 ? 1024 : PAGE;      // LDS bytes reserved per page
+  static constexpr int NINSTR = SLOT / 1024;                  // DMA instructions per page
+  // LDS byte of row-relative byte `byte` of row `row`
+  __device__ static __forceinline__ int at(int row, int byte) {
+    return row * RB + (((byte >> 4) ^ (row & SWZ)) << 4) + (byte & 15);
+  }
+  // page byte lane `lane` of DMA instruction t fetches (its LDS position is 1024t + 16 lane)
+  __device__ static __forceinline__ int src(int t, int lane) {
+    const int pos = 64 * t + lane;                 // 16-byte chunk index in the slot
+    const int row = pos / CPR, cs = pos % CPR;
+    return row * RB + ((cs ^ (row & SWZ)) << 4);   // rows >= 16 fall outside the page: read as 0
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+
+// LDS reads of DMA-filled stages are issued as inline assembly: the compiler cannot
+// tell the ring stages apart and would otherwise wait for every DMA in flight
+// (vmcnt(0)) before each read.  The explicit vmcnt waits of the ring order the
+// reads after their own stage's DMA; lds_fence(regs) waits for the reads
+// (lgkmcnt(0)) and ties the registers to that wait so no use can move above it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8_t*)p;
+}
+__device__ __forceinline__ u32x4 ds_b128(uint32_t a) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+__device__ __forceinline__ u32x2 ds_b64(uint32_t a) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+__device__ __forceinline__ uint32_t ds_b32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+__device__ __forceinline__ uint32_t ds_u16(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void lds_tie(T& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in [3:0] and [15:14]; expcnt and
+// lgkmcnt fields left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int LPR, int NST>
+__device__ __forceinline__ void wait_rounds_after(int rounds_after) {
+  // rounds_after in [0, NST-1]: the loads of that many later rounds may stay in flight
+  static_assert(NST <= 5, "wait table");
+  if (rounds_after <= 0) wait_vmcnt<0>();
+  else if (rounds_after == 1) wait_vmcnt<(1 * LPR < 63 ? 1 * LPR : 63)>();
+  else if (rounds_after == 2) wait_vmcnt<(2 * LPR < 63 ? 2 * LPR : 63)>();
+  else if (rounds_after == 3) wait_vmcnt<(3 * LPR < 63 ? 3 * LPR : 63)>();
+  else wait_vmcnt<(4 * LPR < 63 ? 4 * LPR : 63)>();
 }
 
 // lazy rescaling: the exponent reference of a head moves only when a logit exceeds
@@ -462,12 +555,28 @@ __device__ __forceinline__ Round<CH> fetch_round(const Params& p, BlockIds& ids,
 // and the accumulators are rescaled only when a head's maximum jumps.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int KT, int VT, int D, int CH>
+template <int KT, int VT, int D, int CH, int NST>
+struct StageGeo {
+  using KP = LdsPage<KT, D>;
+  using VP = LdsPage<VT, D>;
+  static constexpr bool META = (KT == DT_INT4);           // INT4 is K and V together
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = CH * KP::SLOT;
+  static constexpr int M_OFF = V_OFF + CH * VP::SLOT;     // per page: K meta [0,256), V meta [256,512)
+  static constexpr int STAGE = M_OFF + (META ? CH * 512 : 0);
+  static constexpr int BYTES = NST * STAGE;
+  static constexpr int LPR = CH * (KP::NINSTR + VP::NINSTR + (META ? 2 : 0));   // DMA loads per round
+};
+
+template <int KT, int VT, int D, int CH, int NST>
 __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
   using KG = Geo<KT, D>;
   using VG = Geo<VT, D>;
-  constexpr int NS = D / 32;       // QK k-steps
+  using SG = StageGeo<KT, VT, D, CH, NST>;
+  using KP = typename SG::KP;
+  using VP = typename SG::VP;
+  constexpr int NS = D / 32;       // QK k-steps (fp16 / bf16 path)
   constexpr int NE = VG::kNE;      // PV n-tiles
   constexpr bool KBF = (KT == DT_BF16);
   constexpr bool VBF = (VT == DT_BF16);
@@ -478,9 +587,23 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   // offset times sum_t p_t is removed after the product, with sum_t p_t taken from
   // one more MFMA against a column of ones (the same rounded p the product saw)
   constexpr bool V_FOLD = (VT == DT_INT8 || VT == DT_INT4);
-  constexpr float V_OFF = (VT == DT_INT8) ? 1152.0f : 1024.0f;
-  constexpr int KPAGE = 16 * KG::kRowBytes;   // bytes of one (block, head) K page
-  constexpr int VPAGE = 16 * VG::kRowBytes;
+  constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 1024.0f;
+  constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
+
+  // one LDS object per ring stage: reads of one stage then carry no dependence on
+  // the DMA still filling another, so only the waits the pipeline needs are emitted
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[SG::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[SG::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[NST > 2 ? SG::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[NST > 3 ? SG::STAGE : 16];
+  auto stage_ptr = [&](auto s_tag) -> uint8_t* {
+    constexpr int S = decltype(s_tag)::value;
+    if constexpr (S == 0) return lds0;
+    else if constexpr (S == 1) return lds1;
+    else if constexpr (S == 2) return lds2;
+    else return lds3;
+  };
 
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
@@ -507,74 +630,83 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   const int n_pages = (tok_end - tok0 + 15) >> 4;
   const int pg0 = tok0 >> 4;
   const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int n_rounds = (n_pages + CH - 1) / CH;
 
+  // ---- the query operand and the scales, loaded before any DMA is in flight (a
+  //      wait on a later load would also wait for every DMA issued before it) ----
   // ---- query operand: head c (zero if c >= g), in the k order of the K operand ----
   u32x4 qop[NS];
-  float qsum = 0.0f;
-  // integer path: q = sq * (qh + ql / 256) with int8 qh, ql and a per-head scale
-  // sq = max|q| / 127 (a 16-bit fixed-point q; error <= 2^-8 sq per element)
-  u32x4 qhi[KI8 ? NSI : 1], qlo[KI8 ? NSI : 1];
+  // integer path: q = sq * (q2 + q1 / 128 + q0 / 16384), three int8 digits and a
+  // per-head scale sq = max|q| / 127; each digit's remainder lies in [-64, 64], so
+  // no digit clips, and the representation error is below 2^-15 sq per element
+  u32x4 qd[KI8 ? 3 : 1][KI8 ? NSI : 1];
   float sq = 1.0f;
-  float qsum_i = 0.0f;   // INT4: 256 * sum(qh) + sum(ql) of head c
-  if constexpr (KI8) {
+  float qsum_i = 0.0f;   // INT4: sum over d of (16384 q2 + 128 q1 + q0) for head c
+  {
     const bool hv = c < g;
     const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * g + (hv ? c : 0)) * D;
-    float qv[NSI][16];
-    float amax = 0.0f;
+    if constexpr (KI8) {
+      float qv[NSI][16];
+      float amax = 0.0f;
 #pragma unroll
-    for (int s2 = 0; s2 < NSI; ++s2)
+      for (int s2 = 0; s2 < NSI; ++s2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        qv[s2][e] = hv ? bf16_bits_to_f32(qrow[k_dim_i8<KT, D>(qg, s2, e)]) : 0.0f;
-        amax = fmaxf(amax, fabsf(qv[s2][e]));
-      }
-    amax = fmaxf(amax, shfl_xor_f(amax, 16));
-    amax = fmaxf(amax, shfl_xor_f(amax, 32));
-    sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
-    const float inv = 1.0f / sq;
-    int sh = 0, sl = 0;
-#pragma unroll
-    for (int s2 = 0; s2 < NSI; ++s2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t wh = 0, wl = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x = qv[s2][4 * i + k] * inv;
-          const float h = fminf(fmaxf(rintf(x), -127.0f), 127.0f);
-          const float l = fminf(fmaxf(rintf((x - h) * 256.0f), -127.0f), 127.0f);
-          wh |= ((uint32_t)(int32_t)h & 0xffu) << (8 * k);
-          wl |= ((uint32_t)(int32_t)l & 0xffu) << (8 * k);
-          sh += (int)h;
-          sl += (int)l;
+        for (int e = 0; e < 16; ++e) {
+          qv[s2][e] = bf16_bits_to_f32(qrow[k_dim_i8<KT, D>(qg, s2, e)]);
+          if (!hv) qv[s2][e] = 0.0f;
+          amax = fmaxf(amax, fabsf(qv[s2][e]));
         }
-        qhi[s2][i] = wh;
-        qlo[s2][i] = wl;
+      amax = fmaxf(amax, shfl_xor_f(amax, 16));
+      amax = fmaxf(amax, shfl_xor_f(amax, 32));
+      sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
+      const float inv = 1.0f / sq;
+      int dsum[3] = {0, 0, 0};
+#pragma unroll
+      for (int s2 = 0; s2 < NSI; ++s2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float x = fminf(fmaxf(qv[s2][4 * i + k] * inv, -127.0f), 127.0f);
+#pragma unroll
+            for (int dg = 0; dg < 3; ++dg) {
+              const float digit = rintf(x);
+              x = (x - digit) * 128.0f;
+              w[dg] |= ((uint32_t)(int32_t)digit & 0xffu) << (8 * k);
+              dsum[dg] += (int)digit;
+            }
+          }
+#pragma unroll
+          for (int dg = 0; dg < 3; ++dg) qd[dg][s2][i] = w[dg];
+        }
       }
-    }
-    if constexpr (KT == DT_INT4) {
-      sh += __shfl_xor(sh, 16, 64);
-      sh += __shfl_xor(sh, 32, 64);
-      sl += __shfl_xor(sl, 16, 64);
-      sl += __shfl_xor(sl, 32, 64);
-      qsum_i = (float)(256 * sh + sl);
-    }
-  } else {
-    const bool hv = c < g;
-    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * g + (hv ? c : 0)) * D;
+      if constexpr (KT == DT_INT4) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      uint32_t qb[8];
+        for (int dg = 0; dg < 3; ++dg) {
+          dsum[dg] += __shfl_xor(dsum[dg], 16, 64);
+          dsum[dg] += __shfl_xor(dsum[dg], 32, 64);
+        }
+        qsum_i = (float)(dsum[0] * 128 + dsum[1]) * 128.0f + (float)dsum[2];
+      }
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[e] = hv ? (uint32_t)qrow[k_dim<KT, D>(qg, s, e)] : 0u;
+      for (int s = 0; s < NS; ++s) {
+        uint32_t qb[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (KBF) {
-          qop[s][i] = qb[2 * i] | (qb[2 * i + 1] << 16);
-        } else {
-          f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(qb[2 * i]),
-                                                                          bf16_bits_to_f32(qb[2 * i + 1])));
-          qop[s][i] = __builtin_bit_cast(uint32_t, h2);
+        for (int e = 0; e < 8; ++e) {
+          qb[e] = (uint32_t)qrow[k_dim<KT, D>(qg, s, e)];
+          if (!hv) qb[e] = 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (KBF) {
+            qop[s][i] = qb[2 * i] | (qb[2 * i + 1] << 16);
+          } else {
+            f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(qb[2 * i]),
+                                                                            bf16_bits_to_f32(qb[2 * i + 1])));
+            qop[s][i] = __builtin_bit_cast(uint32_t, h2);
+          }
         }
       }
     }
@@ -584,9 +716,62 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   if constexpr (KT == DT_INT8 || KT == DT_E4M3 || KT == DT_E5M2) {
     if (p.k_scale) kfac *= p.k_scale[p.k_scale_per_head ? kvh : 0];
   }
-  // integer path: logit = kfac * sq / 256 * (256 acc_hi + acc_lo)
-  const float kq = kfac * sq * (1.0f / 256.0f);
-  const float kq4 = p.sm_log2 * sq * (1.0f / 256.0f);   // INT4: times the token's scale
+  // integer path: logit = kfac * sq / 16384 * (16384 a2 + 128 a1 + a0)
+  const float kq = kfac * sq * (1.0f / 16384.0f);
+  const float kq4 = p.sm_log2 * sq * (1.0f / 16384.0f);   // INT4: times the token's scale
+  float vfac = 1.0f;
+  if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
+    if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
+  }
+
+  // ---- block ids of the first rounds and their DMA, then the ring ----
+  // block ids are scalar loads (the table is read-only here), counted by lgkmcnt
+  // and never by the vmcnt the ring waits on
+  const_i32_t* cbt = (const_i32_t*)(bt + pg0);
+  int bad = 0;                                 // pages with an out-of-range block id
+  Round<CH> rd[NST];
+  int koff[KP::NINSTR], voff[VP::NINSTR];
+#pragma unroll
+  for (int t = 0; t < KP::NINSTR; ++t) koff[t] = KP::src(t, lane);
+#pragma unroll
+  for (int t = 0; t < VP::NINSTR; ++t) voff[t] = VP::src(t, lane);
+  const size_t head_pages = (size_t)p.Hkv;     // pages of one block: one per KV head
+
+  auto issue = [&](const Round<CH>& r, auto s_tag) {
+    uint8_t* sb = stage_ptr(s_tag);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const size_t pidx = (size_t)r.bid[i] * head_pages + kvh;
+      const auto rk = page_rsrc(p.k_pages + pidx * KPAGE, r.ok[i] ? KPAGE : 0);
+#pragma unroll
+      for (int t = 0; t < KP::NINSTR; ++t) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
+      const auto rv = page_rsrc(p.v_pages + pidx * VPAGE, r.ok[i] ? VPAGE : 0);
+#pragma unroll
+      for (int t = 0; t < VP::NINSTR; ++t) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
+      if constexpr (SG::META) {
+        const auto rkm = page_rsrc(p.k_meta + pidx * 32, r.ok[i] ? 128 : 0);
+        dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
+        const auto rvm = page_rsrc(p.v_meta + pidx * 32, r.ok[i] ? 128 : 0);
+        dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
+      }
+    }
+  };
+  auto fetch = [&](int first) {
+    Round<CH> r;
+    r.np = min(CH, n_pages - first);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int bb = cbt[min(first + i, n_pages - 1)];
+      const bool inb = (bb >= 0) && (bb < p.num_blocks);
+      r.ok[i] = (i < r.np) && inb;
+      r.bid[i] = r.ok[i] ? bb : 0;
+      if (i < r.np && !inb) bad++;
+    }
+    return r;
+  };
+  if (0 < n_rounds) { rd[0] = fetch(0); issue(rd[0], std::integral_constant<int, 0>{}); }
+  if (NST > 2 && 1 < n_rounds) { rd[1] = fetch(CH); issue(rd[1], std::integral_constant<int, 1>{}); }
+  if (NST > 3 && 2 < n_rounds) { rd[2] = fetch(2 * CH); issue(rd[2], std::integral_constant<int, 2>{}); }
 
   // ---- wave state ----
   float m_ref = -INFINITY;   // exponent reference of head c (uniform over qg)
@@ -597,85 +782,78 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   for (int e = 0; e < NE; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};   // V_FOLD: sum_t p_t per head (all columns alike)
 
-  const size_t head_pages = (size_t)p.Hkv;                        // pages of one block: one per KV head
-  const int k_off = c * KG::kRowBytes + qg * KG::kPS;             // this lane's first K piece in a page
-  const int v_off = 4 * qg * VG::kRowBytes + c * VG::kVRowBytes;  // ... V bytes of its first row
-  const int meta_off = 4 * qg * 8;                                 // (s, zp) of tokens 4qg..4qg+3
-
-  // ---- K loads of one round ----
-  uint32_t kw[CH][KG::kKDw];
-  float4 kmeta[CH][2];
-  auto load_k = [&](const Round<CH>& r) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const size_t pidx = (size_t)r.bid[i] * head_pages + kvh;
-      const auto rs = page_rsrc(p.k_pages + pidx * KPAGE, r.ok[i] ? KPAGE : 0);
-#pragma unroll
-      for (int j = 0; j < KG::kNPC; ++j) {
-        uint32_t piece[KG::kPS / 4];
-        buf_load<KG::kPS / 4>(piece, rs, k_off + j * 4 * KG::kPS);
-#pragma unroll
-        for (int t = 0; t < KG::kPS / 4; ++t) kw[i][j * (KG::kPS / 4) + t] = piece[t];
-      }
-      if constexpr (KT == DT_INT4) {
-        const auto rm = page_rsrc(p.k_meta + pidx * 32, r.ok[i] ? 128 : 0);
-        kmeta[i][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off, 0, 0));
-        kmeta[i][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off + 16, 0, 0));
-      }
-    }
-  };
-
-  // ---- one round: V loads, QK, (next K loads), softmax, PV ----
+  // ---- one round from LDS stage `stage`: QK, softmax, PV ----
   // TAIL: the partition's last round, the only one with pages past the end or a
   // partial page; full rounds skip every per-token test.
-  auto round = [&](auto tail_tag, Round<CH>& cur, BlockIds& ids, int first) {
+  auto round = [&](auto tail_tag, const Round<CH>& cur, auto s_tag, int first) {
     constexpr bool TAIL = decltype(tail_tag)::value;
-    uint32_t vw[CH][4][VG::kVDw];
-    float4 vmeta[CH][2];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const size_t pidx = (size_t)cur.bid[i] * head_pages + kvh;
-      const auto rs = page_rsrc(p.v_pages + pidx * VPAGE, cur.ok[i] ? VPAGE : 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) buf_load_v_row<VT, D>(vw[i][r], rs, v_off + r * VG::kRowBytes);
-      if constexpr (VT == DT_INT4) {
-        const auto rm = page_rsrc(p.v_meta + pidx * 32, cur.ok[i] ? 128 : 0);
-        vmeta[i][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off, 0, 0));
-        vmeta[i][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, meta_off + 16, 0, 0));
-      }
-    }
-    Round<CH> nxt;
-    if constexpr (!TAIL) nxt = fetch_round<CH>(p, ids, first + CH);
+    const uint8_t* sb = stage_ptr(s_tag);
 
     // QK: logits of head c for tokens 4qg+r of each page
     float sl[CH][4];
     float cmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
+      const uint32_t kb = lds_addr(sb + SG::K_OFF + i * KP::SLOT);
+      uint32_t kw[KG::kKDw];
+      float4 km0, km1;
+      {
+        u32x4 kv16[KG::kNPC];
+        u32x2 kv8[KG::kNPC];
+#pragma unroll
+        for (int j = 0; j < KG::kNPC; ++j) {
+          const uint32_t at = kb + KP::at(c, j * 4 * KG::kPS + qg * KG::kPS);
+          if constexpr (KG::kPS == 16) kv16[j] = ds_b128(at);
+          else kv8[j] = ds_b64(at);
+        }
+        u32x4 m0, m1;
+        if constexpr (KT == DT_INT4) {
+          const uint32_t mb = lds_addr(sb + SG::M_OFF + i * 512 + 32 * qg);
+          m0 = ds_b128(mb);
+          m1 = ds_b128(mb + 16);
+        }
+        lds_fence();
+#pragma unroll
+        for (int j = 0; j < KG::kNPC; ++j) {
+          if constexpr (KG::kPS == 16) {
+            lds_tie(kv16[j]);
+            kw[4 * j] = kv16[j][0]; kw[4 * j + 1] = kv16[j][1]; kw[4 * j + 2] = kv16[j][2]; kw[4 * j + 3] = kv16[j][3];
+          } else {
+            lds_tie(kv8[j]);
+            kw[2 * j] = kv8[j][0]; kw[2 * j + 1] = kv8[j][1];
+          }
+        }
+        if constexpr (KT == DT_INT4) {
+          lds_tie(m0);
+          lds_tie(m1);
+          km0 = __builtin_bit_cast(float4, m0);
+          km1 = __builtin_bit_cast(float4, m1);
+        }
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (KI8) {
-        i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+        i32x4 a2 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a0 = {0, 0, 0, 0};
 #pragma unroll
         for (int s2 = 0; s2 < NSI; ++s2) {
-          const u32x4 ko = k_operand_i8<KT, D>(kw[i], s2);
-          ah = mfma_i8(ko, qhi[s2], ah);
-          al = mfma_i8(ko, qlo[s2], al);
+          const u32x4 ko = k_operand_i8<KT, D>(kw, s2);
+          a2 = mfma_i8(ko, qd[0][s2], a2);
+          a1 = mfma_i8(ko, qd[1][s2], a1);
+          a0 = mfma_i8(ko, qd[2][s2], a0);
         }
+        // (128 a2 + a1) is exact in int32; the last digit joins in float32
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = (float)((ah[r] << 8) + al[r]);   // exact in int32
+        for (int r = 0; r < 4; ++r) acc[r] = (float)((a2[r] << 7) + a1[r]) * 128.0f + (float)a0[r];
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2) acc = mfma_qk<KBF>(k_operand<KT, D>(kw[i], s2), qop[s2], acc);
+        for (int s2 = 0; s2 < NS; ++s2) acc = mfma_qk<KBF>(k_operand<KT, D>(kw, s2), qop[s2], acc);
       }
       const int tbase = tok0 + (first + i) * 16 + 4 * qg;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float z;
         if constexpr (KT == DT_INT4) {
-          const float ks = (r < 2) ? ((r == 0) ? kmeta[i][0].x : kmeta[i][0].z)
-                                   : ((r == 2) ? kmeta[i][1].x : kmeta[i][1].z);
-          const float kz = (r < 2) ? ((r == 0) ? kmeta[i][0].y : kmeta[i][0].w)
-                                   : ((r == 2) ? kmeta[i][1].y : kmeta[i][1].w);
+          const float ks = (r < 2) ? ((r == 0) ? km0.x : km0.z) : ((r == 2) ? km1.x : km1.z);
+          const float kz = (r < 2) ? ((r == 0) ? km0.y : km0.w) : ((r == 2) ? km1.y : km1.w);
           z = (ks * kq4) * (acc[r] - kz * qsum_i);
         } else if constexpr (KT == DT_INT8) {
           z = acc[r] * kq;
@@ -689,9 +867,6 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         cmax = fmaxf(cmax, z);
       }
     }
-
-    // K of the next round: the K registers are free now
-    if constexpr (!TAIL) load_k(nxt);
 
     // lazy online-softmax update
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
@@ -732,9 +907,47 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
           l_run += pr[r];
         }
         uint32_t a0, a1;
+        // V rows 4qg..4qg+3 of the page, this lane's columns (and INT4 metadata)
+        const uint32_t vb = lds_addr(sb + SG::V_OFF + pi * VP::SLOT);
+        uint32_t vw[4][VG::kVDw];
+        u32x4 vraw16[4];
+        u32x2 vraw8[4];
+        uint32_t vraw4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t at = vb + VP::at(4 * qg + r, c * VG::kVRowBytes);
+          if constexpr (VG::kVRowBytes == 16) vraw16[r] = ds_b128(at);
+          else if constexpr (VG::kVRowBytes == 8) vraw8[r] = ds_b64(at);
+          else if constexpr (VG::kVRowBytes == 4) vraw4[r] = ds_b32(at);
+          else vraw4[r] = ds_u16(at);
+        }
+        u32x4 vm0r, vm1r;
         if constexpr (VT == DT_INT4) {
-          const float vs[4] = {vmeta[pi][0].x, vmeta[pi][0].z, vmeta[pi][1].x, vmeta[pi][1].z};
-          const float vz[4] = {vmeta[pi][0].y, vmeta[pi][0].w, vmeta[pi][1].y, vmeta[pi][1].w};
+          const uint32_t mb = lds_addr(sb + SG::M_OFF + pi * 512 + 256 + 32 * qg);
+          vm0r = ds_b128(mb);
+          vm1r = ds_b128(mb + 16);
+        }
+        lds_fence();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (VG::kVRowBytes == 16) {
+            lds_tie(vraw16[r]);
+            vw[r][0] = vraw16[r][0]; vw[r][1] = vraw16[r][1]; vw[r][2] = vraw16[r][2]; vw[r][3] = vraw16[r][3];
+          } else if constexpr (VG::kVRowBytes == 8) {
+            lds_tie(vraw8[r]);
+            vw[r][0] = vraw8[r][0]; vw[r][1] = vraw8[r][1];
+          } else {
+            lds_tie(vraw4[r]);
+            vw[r][0] = vraw4[r];
+          }
+        }
+        if constexpr (VT == DT_INT4) {
+          lds_tie(vm0r);
+          lds_tie(vm1r);
+          const float4 vm0 = __builtin_bit_cast(float4, vm0r);
+          const float4 vm1 = __builtin_bit_cast(float4, vm1r);
+          const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
+          const float vz[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
           float ps[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ps[r] = (pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
@@ -758,7 +971,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
           aop_lo[2 * h2 + 1] = (c < g) ? l1 : 0u;
         }
 
-        v_operands<VT, D>(vw[pi], vop[h2]);
+        v_operands<VT, D>(vw, vop[h2]);
         if constexpr (TAIL && V_NAN) {
           // tokens past the end of the sequence: their slots may hold NaN codes
           const int tb = tok0 + (first + pi) * 16 + 4 * qg;
@@ -782,20 +995,28 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         sacc = mfma_pv2<false>(aop, ones, sacc);
       }
     }
-    if constexpr (!TAIL) cur = nxt;
   };
 
-  // ---- prologue: block ids and K of the first round; then the rounds ----
-  BlockIds ids;
-  ids.bt = bt + pg0;
-  ids.n_pages = n_pages;
-  ids.cur = load_window(ids, 0);
-  ids.nxt = load_window(ids, 1);
-  Round<CH> cur = fetch_round<CH>(p, ids, 0);
-  load_k(cur);
-  const int n_rounds = (n_pages + CH - 1) / CH;
-  for (int rr = 0; rr + 1 < n_rounds; ++rr) round(std::false_type{}, cur, ids, rr * CH);
-  round(std::true_type{}, cur, ids, (n_rounds - 1) * CH);
+  // ---- the rounds: issue round r+NST-1, wait for round r, compute round r; the loop
+  //      is unrolled by NST so that every stage index is a constant ----
+  auto step = [&](auto s_tag, int r) {
+    constexpr int S = decltype(s_tag)::value;
+    constexpr int SA = (S + NST - 1) % NST;          // stage of round r + NST - 1
+    if (r + NST - 1 < n_rounds) {
+      rd[SA] = fetch((r + NST - 1) * CH);
+      issue(rd[SA], std::integral_constant<int, SA>{});
+    }
+    wait_rounds_after<SG::LPR, NST>(min(NST - 1, n_rounds - 1 - r));
+    if (r + 1 < n_rounds) round(std::false_type{}, rd[S], s_tag, r * CH);
+    else round(std::true_type{}, rd[S], s_tag, r * CH);
+  };
+  for (int r = 0; r < n_rounds; r += NST) {
+    step(std::integral_constant<int, 0>{}, r);
+    if (r + 1 < n_rounds) step(std::integral_constant<int, 1>{}, r + 1);
+    if constexpr (NST > 2) if (r + 2 < n_rounds) step(std::integral_constant<int, 2 % NST>{}, r + 2);
+    if constexpr (NST > 3) if (r + 3 < n_rounds) step(std::integral_constant<int, 3 % NST>{}, r + 3);
+  }
+  if (bad && p.err && lane == 0) atomicAdd(p.err, bad);
 
   // ---- full softmax sums over the lane groups ----
   l_run += shfl_xor_f(l_run, 16);
@@ -803,11 +1024,6 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   if constexpr (VT == DT_INT4) {
     corr_run += shfl_xor_f(corr_run, 16);
     corr_run += shfl_xor_f(corr_run, 32);
-  }
-
-  float vfac = 1.0f;
-  if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
-    if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
   }
 
   // lane (qg, c) holds O[head 4qg+r][d = NE*c + e]; fetch that head's sums
@@ -827,7 +1043,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       float v = oacc[e][r] - ch[r];
-      if constexpr (V_FOLD) v -= V_OFF * sacc[r];
+      if constexpr (V_FOLD) v -= V_OFFSET * sacc[r];
       o[e] = v * vfac;
     }
     if (single) {
@@ -861,15 +1077,21 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
 // dispatch
 // ---------------------------------------------------------------------------
 
-// pages a wave streams per round (K of the next round is in flight meanwhile)
+// pages per round and rounds in the LDS ring (the ring holds NST-1 rounds in
+// flight while one is consumed)
 template <int KT, int VT>
 constexpr int pages_per_round() {
-  return (KT == DT_BF16 || VT == DT_BF16) ? 2 : 4;
+  return 2;
+}
+template <int KT, int VT>
+constexpr int ring_stages() {
+  return 2;
 }
 
 template <int KT, int VT, int D>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, D, pages_per_round<KT, VT>()>), grid, dim3(64), 0, s, prm);
+  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, D, pages_per_round<KT, VT>(), ring_stages<KT, VT>()>), grid,
+                     dim3(64), 0, s, prm);
   return hipGetLastError();
 }
 
