@@ -167,7 +167,7 @@ class GpuWorkload:
             if km is not None:
                 s.k_meta, s.v_meta = km.data_ptr(), vm.data_ptr()
             self.structs.append(s)
-        ws = kvq.kvq_decode_workspace_size(w.B, w.Hq, w.D, inp.max_seq_len, w.partition)
+        ws = kvq.kvq_decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, inp.max_seq_len, w.partition)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
         self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=device)
         self.kv_bytes = kv_bytes(inp)

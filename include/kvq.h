@@ -158,14 +158,15 @@ kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const 
 
 /*
  * kvq_decode_workspace_size — bytes of device workspace kvq_paged_attention_decode
- * needs for these sizes (0 when every sequence fits one partition).
- * partition = 0 selects the default (512 tokens).  Layout, for reference:
- * float32 max [batch][num_q_heads][P], sum [batch][num_q_heads][P] and
- * accumulators [batch][num_q_heads][P][head_dim] (P = ceil(max_seq_len /
- * partition)), each region 16-byte aligned.
+ * needs for these sizes and this partition (0 when the decode runs as a single
+ * chunk; also 0 for invalid arguments).  Layout, for reference, with
+ * S = n_chunks + batch piece slots (n_chunks as described under `partition`
+ * below): float32 max [S][num_q_heads], sum [S][num_q_heads], int32 chunk range
+ * [batch][2], float32 accumulators [S][num_q_heads][head_dim], each region
+ * 16-byte aligned.
  */
-size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_seq_len, int32_t partition);
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t partition);
 
 /*
  * kvq_paged_attention_decode — one query token per sequence against the paged
@@ -177,10 +178,19 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
  *     z_i = softmax_scale * sum_c q[b][h][c] * k_hat_i[c]    for i < seq_lens[b]
  *     out[b][h] = sum_i softmax(z)_i * v_hat_i
  * Token position p of sequence b is read from page block_tables[b][p / 16],
- * offset p % 16.  Accumulation is float32.  Sequences are cut into partitions of
- * `partition` tokens (0 = 512); when max_seq_len exceeds it, per-partition
- * (max, sum, accumulator) go to the workspace and a second kernel merges them
- * (split-KV reduce).
+ * offset p % 16.  Accumulation is float32.
+ * Work split: the pages of all sequences, concatenated in sequence order, are
+ * cut into chunks of equal page count, and each (chunk, KV head) is one unit of
+ * work, so every unit streams the same number of bytes whatever the length mix.
+ * A sequence inside one chunk is finished there; a sequence cut by chunk
+ * boundaries leaves one (max, sum, accumulator) partial per piece in the
+ * workspace, and a second kernel merges them (split-KV reduce).
+ *   partition = 0: about 2048 / num_kv_heads chunks, their size fixed on the
+ *                  device from the page total (at least 4 pages);
+ *   partition > 0: chunks of partition / 16 pages, ceil(batch *
+ *                  ceil(max_seq_len / 16) / (partition / 16)) of them launched.
+ * Results of different partitions agree to float32 accumulation order and the
+ * fp16 rounding of the softmax weights (relative 2^-12 per weight).
  *   q             (device) bf16 [batch][num_q_heads][head_dim]; |q| < 65504
  *   block_tables  (device) int32 [batch][max_blocks_per_seq]
  *   seq_lens      (device) int32 [batch]; <= 0 gives a zero output row; values

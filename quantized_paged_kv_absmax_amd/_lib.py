@@ -55,7 +55,7 @@ def load():
     lib.kvq_cache_write.restype = I32
     lib.kvq_convert_cache.argtypes = [CP, P, P, I32, I32, P]
     lib.kvq_convert_cache.restype = I32
-    lib.kvq_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.kvq_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.kvq_decode_workspace_size.restype = SZ
     lib.kvq_paged_attention_decode.argtypes = [CP, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
     lib.kvq_paged_attention_decode.restype = I32

@@ -122,8 +122,9 @@ def kvq_convert_cache(cache, k_src, v_src, first_block=0, num_blocks=None, strea
     check(st, "kvq_convert_cache")
 
 
-def kvq_decode_workspace_size(batch, num_q_heads, head_dim, max_seq_len, partition=0):
-    return int(_lib.load().kvq_decode_workspace_size(batch, num_q_heads, head_dim, max_seq_len, partition))
+def kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition=0):
+    return int(_lib.load().kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                     partition))
 
 
 def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, softmax_scale, partition=0,
@@ -141,7 +142,7 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
     odt = _dt(out_dtype)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32 if odt == _lib.F32 else torch.bfloat16, device=q.device)
-    need = kvq_decode_workspace_size(B, Hq, D, max_seq_len, partition)
+    need = kvq_decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_seq_len, partition)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -59,14 +59,18 @@ struct Params {
   const int32_t* block_tables;
   int max_blocks_per_seq;
   const int32_t* seq_lens;
+  int batch;
   int num_blocks, Hkv, Hq, g;
   int max_seq_len;
-  float sm_log2;  // softmax_scale * log2(e)
-  int partition;
-  int num_partitions;
-  float* ws_m;       // [B][Hq][P] running max (base 2) of each partition
-  float* ws_l;       // [B][Hq][P] softmax sum
-  float* ws_o;       // [B][Hq][P][D] unnormalised output
+  float sm_log2;     // softmax_scale * log2(e)
+  int chunk_pages;   // pages per chunk; 0: ceil(total pages / n_chunks), at least min_chunk, even
+  int n_chunks;      // chunks in the launch (grid x)
+  int min_chunk;
+  int q_slot;        // LDS bytes of one query buffer (g * D * 2 rounded up to 1 KB)
+  float* ws_m;       // [slot][Hq] exponent reference (base 2) of each piece
+  float* ws_l;       // [slot][Hq] softmax sum of each piece
+  float* ws_o;       // [slot][Hq][D] unnormalised output of each piece
+  int2* ws_rec;      // [B] first and last chunk of each sequence
   int out_f32;
   void* out;
   int32_t* err;
@@ -89,7 +93,7 @@ struct Geo {
 
 // row byte offset of dword dw of the K bytes of lane group qg
 template <int DT, int D>
-__device__ __forceinline__ int k_byte(int qg, int dw) {
+__host__ __device__ constexpr int k_byte(int qg, int dw) {
   constexpr int PS = Geo<DT, D>::kPS, DPP = PS / 4;
   return (dw / DPP) * 4 * PS + qg * PS + 4 * (dw % DPP);
 }
@@ -145,7 +149,7 @@ __device__ __forceinline__ u32x4 k_operand(const uint32_t (&kw)[N], int s) {
 
 // head-dim index of operand element e of k-step s for lane group qg (must match k_operand)
 template <int DT, int D>
-__device__ __forceinline__ int k_dim(int qg, int s, int e) {
+__host__ __device__ constexpr int k_dim(int qg, int s, int e) {
   if constexpr (DT == DT_INT4) return 2 * (k_byte<DT, D>(qg, s) + (e & 3)) + (e >> 2);
   else if constexpr (DT == DT_BF16) return (k_byte<DT, D>(qg, 4 * s + (e >> 1)) + 2 * (e & 1)) >> 1;
   else return k_byte<DT, D>(qg, 2 * s + (e >> 2)) + (e & 3);
@@ -167,9 +171,36 @@ __device__ __forceinline__ u32x4 k_operand_i8(const uint32_t (&kw)[N], int s) {
 
 // head-dim index of element e (0..15) of integer-path step s (must match k_operand_i8)
 template <int DT, int D>
-__device__ __forceinline__ int k_dim_i8(int qg, int s, int e) {
+__host__ __device__ constexpr int k_dim_i8(int qg, int s, int e) {
   if constexpr (DT == DT_INT8) return k_byte<DT, D>(qg, 4 * s + (e >> 2)) + (e & 3);
   else return 2 * (k_byte<DT, D>(qg, 2 * s + (e >> 3)) + (e & 3)) + ((e >> 2) & 1);
+}
+
+// The query elements one lane needs for one k-step are a run of RUN contiguous
+// head-dim positions (8 on the fp16 / bf16 path, 16 on the integer path), in an
+// order that does not depend on the lane group, starting on a 16-byte boundary:
+// the query is read from LDS as whole 16-byte pieces.
+template <int DT, int D, bool I8>
+__host__ __device__ constexpr int q_dim(int qg, int s, int e) {
+  if constexpr (I8) return k_dim_i8<DT, D>(qg, s, e);
+  else return k_dim<DT, D>(qg, s, e);
+}
+template <int DT, int D, bool I8>
+constexpr bool q_runs_ok() {
+  constexpr int RUN = I8 ? 16 : 8, NSTEP = I8 ? D / 64 : D / 32;
+  for (int qg = 0; qg < 4; ++qg)
+    for (int s = 0; s < NSTEP; ++s) {
+      const int base = q_dim<DT, D, I8>(qg, s, 0);
+      if (base % 8 != 0) return false;
+      unsigned seen = 0;
+      for (int e = 0; e < RUN; ++e) {
+        const int pos = q_dim<DT, D, I8>(qg, s, e) - base;
+        if (pos < 0 || pos >= RUN || pos != q_dim<DT, D, I8>(0, s, e) - q_dim<DT, D, I8>(0, s, 0)) return false;
+        seen |= 1u << pos;
+      }
+      if (seen != (1u << RUN) - 1u) return false;
+    }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -337,11 +368,13 @@ __device__ __forceinline__ void buf_load_v_row(uint32_t (&r)[N], __amdgpu_buffer
 }
 
 // ---------------------------------------------------------------------------
-// split-KV reduce: one workgroup per (query head, sequence) merges the
-// partitions:  o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j.
-// Lane groups of D/4 lanes (4 columns each) take every NG-th partition with a
-// running maximum, and LDS combines the groups.  A separate launch: the kernel
-// boundary makes every partition's stores visible without a device-wide fence.
+// split-KV reduce: one workgroup per (query head, sequence) merges the pieces of
+// a sequence that chunk boundaries cut:
+//   o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j.
+// Piece j of sequence b (chunk rec.x + j) sits in slot rec.x + j + b.  Lane
+// groups of D/4 lanes (4 columns each) take every NG-th piece with a running
+// maximum, and LDS combines the groups.  A separate launch: the kernel boundary
+// makes every piece's stores visible without a device-wide fence.
 // ---------------------------------------------------------------------------
 
 constexpr int kRedThreads = 256;
@@ -351,21 +384,22 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
   constexpr int LPG = D / 4;                  // lanes per group
   constexpr int NG = kRedThreads / LPG;       // groups
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int L = clamp_len(p, b, false);
-  if (L <= 0) return;                         // the partition kernel wrote the zero row
-  const int P = (L + p.partition - 1) / p.partition;
-  const size_t row = (size_t)b * p.Hq + hq;
-  const float* m = p.ws_m + row * p.num_partitions;
-  const float* l = p.ws_l + row * p.num_partitions;
-  const float* o = p.ws_o + row * p.num_partitions * D;
+  const int2 rec = p.ws_rec[b];
+  if (rec.y <= rec.x) return;                 // one piece: the chunk kernel wrote the row
+  const int P = rec.y - rec.x + 1;
+  const size_t s0 = (size_t)rec.x + b;
+  const float* m = p.ws_m + s0 * p.Hq + hq;
+  const float* l = p.ws_l + s0 * p.Hq + hq;
+  const float* o = p.ws_o + (s0 * p.Hq + hq) * D;
 
   const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = grp; j < P; j += NG) {
-    const float mj = m[j];
-    const float lj = l[j];
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * D + 4 * ln);
+    const float mj = m[(size_t)j * p.Hq];
+    if (mj == -INFINITY) continue;            // a piece with no valid token
+    const float lj = l[(size_t)j * p.Hq];
+    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * p.Hq * D + 4 * ln);
     if (mj > M) {
       const float sc = __builtin_amdgcn_exp2f(M - mj);
       acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
@@ -397,8 +431,9 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
       a.x += f * v.x; a.y += f * v.y; a.z += f * v.z; a.w += f * v.w;
       dd += f * s_den[gi];
     }
-    const float r[4] = {a.x / dd, a.y / dd, a.z / dd, a.w / dd};
-    const size_t oi = row * D + 4 * threadIdx.x;
+    const bool any = dd > 0.0f;                 // no valid token at all: zeros
+    const float r[4] = {any ? a.x / dd : 0.0f, any ? a.y / dd : 0.0f, any ? a.z / dd : 0.0f, any ? a.w / dd : 0.0f};
+    const size_t oi = ((size_t)b * p.Hq + hq) * D + 4 * threadIdx.x;
     if (p.out_f32) {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
     } else {
@@ -410,52 +445,8 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// the partition kernel: one wave per (partition, KV head, sequence)
+// the chunk kernel: one wave per (chunk, KV head)
 // ---------------------------------------------------------------------------
-
-// Block ids of the CH pages of one round (wave-uniform) and their validity.
-template <int CH>
-struct Round {
-  int bid[CH];
-  bool ok[CH];
-  int np;        // pages of this round inside the partition
-  int nbad;      // of those, pages with an out-of-range block id
-};
-
-// Block ids are fetched 64 pages at a time: lane i of a window register holds the
-// id of page 64*w + i of the partition (clamped to the last page), one window
-// ahead of its use, so reading an id is a v_readlane and never waits on memory.
-struct BlockIds {
-  const int32_t* bt;   // this sequence's block table, from the partition's first page
-  int n_pages;
-  int cur, nxt;        // window registers
-};
-
-__device__ __forceinline__ int load_window(const BlockIds& w, int win) {
-  const int pi = min(win * 64 + (int)threadIdx.x, w.n_pages - 1);
-  return w.bt[pi];
-}
-
-template <int CH>
-__device__ __forceinline__ Round<CH> fetch_round_nocount(const Params& p, BlockIds& ids, int first) {
-  static_assert(64 % CH == 0, "rounds never straddle a block-id window");
-  if (first > 0 && (first & 63) == 0) {       // entering the next window
-    ids.cur = ids.nxt;
-    ids.nxt = load_window(ids, (first >> 6) + 1);
-  }
-  Round<CH> r;
-  r.np = min(CH, ids.n_pages - first);
-  r.nbad = 0;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int bb = __builtin_amdgcn_readlane(ids.cur, (first & 63) + i);
-    const bool inb = (bb >= 0) && (bb < p.num_blocks);
-    r.ok[i] = (i < r.np) && inb;
-    r.bid[i] = r.ok[i] ? bb : 0;
-    if (i < r.np && !inb) r.nbad++;
-  }
-  return r;
-}
 
 // ---------------------------------------------------------------------------
 // LDS staging.  A wave streams its partition through an NST-deep ring of LDS
@@ -555,7 +546,7 @@ __device__ __forceinline__ void wait_rounds_after(int rounds_after) {
 // and the accumulators are rescaled only when a head's maximum jumps.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int KT, int VT, int D, int CH, int NST>
+template <int KT, int VT, int D, int CH>
 struct StageGeo {
   using KP = LdsPage<KT, D>;
   using VP = LdsPage<VT, D>;
@@ -564,16 +555,45 @@ struct StageGeo {
   static constexpr int V_OFF = CH * KP::SLOT;
   static constexpr int M_OFF = V_OFF + CH * VP::SLOT;     // per page: K meta [0,256), V meta [256,512)
   static constexpr int STAGE = M_OFF + (META ? CH * 512 : 0);
-  static constexpr int BYTES = NST * STAGE;
   static constexpr int LPR = CH * (KP::NINSTR + VP::NINSTR + (META ? 2 : 0));   // DMA loads per round
 };
 
-template <int KT, int VT, int D, int CH, int NST>
-__global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
+// One round: up to CH consecutive pages of one sequence, all inside one segment
+// (the piece of a sequence that lies in this wave's chunk).  Wave-uniform, kept
+// small: three of them are live at once in scalar registers.
+template <int CH>
+struct Desc {
+  int b;          // sequence
+  int pg;         // first page of the round, counted from the start of the sequence
+  int L;          // sequence length in tokens
+  int info;       // kNp: pages in the round (0: no round, the chunk is done); flags below
+  int bid[CH];    // block id of each page, -1: not loaded (past the segment or out of range)
+};
+constexpr int kNp = 3;           // info bits 0-1
+constexpr int kFirst = 1 << 2;   // first round of its segment
+constexpr int kLast = 1 << 3;    // last round of its segment
+constexpr int kTail = 1 << 4;    // holds the sequence's last page (tokens past L are masked)
+constexpr int kWhole = 1 << 5;   // the segment is the whole sequence
+constexpr int kQBuf = 1 << 6;    // query buffer of the segment (segments alternate)
+
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+template <int KT, int VT, int D, int CH>
+__global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
   using KG = Geo<KT, D>;
   using VG = Geo<VT, D>;
-  using SG = StageGeo<KT, VT, D, CH, NST>;
+  using SG = StageGeo<KT, VT, D, CH>;
   using KP = typename SG::KP;
   using VP = typename SG::VP;
   constexpr int NS = D / 32;       // QK k-steps (fp16 / bf16 path)
@@ -590,95 +610,295 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
   constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 1024.0f;
   constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
 
-  // one LDS object per ring stage: reads of one stage then carry no dependence on
-  // the DMA still filling another, so only the waits the pipeline needs are emitted
-  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  // two ring stages, one LDS object each: reads of one stage then carry no
+  // dependence on the DMA still filling the other; the query rows of the current
+  // and the next segment sit in two dynamic-LDS buffers of p.q_slot bytes
   __shared__ __attribute__((aligned(16))) uint8_t lds0[SG::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[SG::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[NST > 2 ? SG::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[NST > 3 ? SG::STAGE : 16];
+  extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
   auto stage_ptr = [&](auto s_tag) -> uint8_t* {
-    constexpr int S = decltype(s_tag)::value;
-    if constexpr (S == 0) return lds0;
-    else if constexpr (S == 1) return lds1;
-    else if constexpr (S == 2) return lds2;
-    else return lds3;
+    if constexpr (decltype(s_tag)::value == 0) return lds0;
+    else return lds1;
   };
 
-  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int w = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x;
   const int c = lane & 15, qg = lane >> 4;
   const int g = p.g;
+  const int B = p.batch;
+  const int cap = min(p.max_seq_len, p.max_blocks_per_seq * 16);
+  const bool counter = (w == 0 && kvh == 0);   // the one wave that counts clamped lengths
 
-  // the length is the same for the whole wave: keep it (and all that derives
-  // from it: page counts, validity, buffer descriptors) in scalar registers
-  const int L = __builtin_amdgcn_readfirstlane(clamp_len(p, b, part == 0 && kvh == 0 && lane == 0));
-  const int tok0 = part * p.partition;
-  const bool single = (p.num_partitions == 1);
+  // length of sequence b, clamped to [0, cap] (0 past the batch)
+  auto load_len = [&](int b, bool count) {
+    int L = 0;
+    if (b < B) {
+      L = p.seq_lens[b];
+      if (L > cap) {
+        if (count && p.err) atomicAdd(p.err, 1);
+        L = cap;
+      }
+      L = max(L, 0);
+    }
+    return L;
+  };
 
-  if (L <= 0 || tok0 >= L) {
-    if (part == 0 && L <= 0) {
+  // ---- pages of every sequence: their total T fixes the chunk size ----
+  int T = 0;
+  int l0 = 0, n0 = 0, i0 = 0;   // B <= 64: length, pages, inclusive page prefix of sequence `lane`
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int L = load_len(b0 + lane, counter);
+    const int np = (L + 15) >> 4;
+    const int inc = wave_incl_sum(np);
+    if (b0 == 0) { l0 = L; n0 = np; i0 = inc; }
+    T += __builtin_amdgcn_readlane(inc, 63);
+  }
+  int C = p.chunk_pages;
+  if (C == 0) C = (max(p.min_chunk, (T + p.n_chunks - 1) / p.n_chunks) + 1) & ~1;
+  const int n_act = max(1, (T + C - 1) / C);
+  if (w >= n_act) return;
+  const int x0 = w * C, x1 = min(x0 + C, T);
+  const bool last_chunk = (w == n_act - 1);
+
+  // ---- the chunk's first sequence: the first whose pages reach past x0, or an
+  //      empty one at or after x0 (empty sequences belong to the chunk holding
+  //      their position; those at the very end to the last chunk) ----
+  auto starts_here = [&](int np, int inc) { return inc > x0 || (np == 0 && inc >= x0); };
+  int bs = 0, ex_bs = 0;
+  if (B <= 64) {
+    const uint64_t before = __builtin_amdgcn_ballot_w64(lane < B && !starts_here(n0, i0));
+    bs = popc64(before);
+    ex_bs = __builtin_amdgcn_readlane(i0 - n0, bs & 63);
+  } else {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int L = load_len(b0 + lane, false);
+      const int np = (L + 15) >> 4;
+      const int inc = carry + wave_incl_sum(np);
+      const int cnt = popc64(__builtin_amdgcn_ballot_w64(lane < B - b0 && !starts_here(np, inc)));
+      if (cnt < min(64, B - b0)) {
+        bs = b0 + cnt;
+        ex_bs = __builtin_amdgcn_readlane(inc - np, cnt);
+        break;
+      }
+      carry = __builtin_amdgcn_readlane(inc, 63);
+    }
+  }
+
+  // ---- window: lane j describes sequence bs + j ----
+  int wL = 0, wnp = 0, wex = 0, wlo = 0, whi = 0;
+  int nwin = 0;
+  bool more = false;
+  auto make_window = [&](bool from_regs) {
+    const int sb = bs + lane;
+    const bool wv = sb < B;
+    if (from_regs) {
+      const int src = sb & 63;
+      wL = __shfl(l0, src, 64);
+      wnp = __shfl(n0, src, 64);
+      wex = __shfl(i0 - n0, src, 64);
+    } else {
+      wL = load_len(sb, false);
+      wnp = (wL + 15) >> 4;
+      wex = ex_bs + wave_incl_sum(wnp) - wnp;
+    }
+    if (!wv) wL = wnp = 0;
+    const bool in_chunk = wv && (last_chunk || wex < x1);
+    wlo = in_chunk ? max(x0 - wex, 0) : 0;
+    whi = in_chunk ? min(x1 - wex, wnp) : 0;
+    nwin = popc64(__builtin_amdgcn_ballot_w64(in_chunk));
+    more = (nwin == 64) && (bs + 64 < B);
+    // records for the reduce: the KV-head-0 wave holding a sequence's last page
+    // stores the range of chunks the sequence spans (equal ends: not split)
+    if (p.ws_rec && kvh == 0 && in_chunk) {
+      int2 rec;
+      if (wnp == 0) rec = make_int2(w, w);
+      else rec = make_int2(wex / C, (wex + wnp - 1) / C);
+      if (wnp == 0 || wex + wnp <= x1) p.ws_rec[sb] = rec;
+    }
+    // empty sequences of the chunk: zero rows for this KV head's query heads
+    uint64_t em = __builtin_amdgcn_ballot_w64(in_chunk && wnp == 0);
+    while (em) {
+      const int j = __builtin_ctzll(em);
+      em &= em - 1;
+      const size_t row0 = ((size_t)(bs + j) * p.Hq + (size_t)kvh * g) * D;
       for (int i = lane; i < g * D; i += 64) {
-        const size_t o = ((size_t)b * p.Hq + (size_t)kvh * g + i / D) * D + (i % D);
-        if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = 0.0f;
-        else reinterpret_cast<uint16_t*>(p.out)[o] = 0;
+        if (p.out_f32) reinterpret_cast<float*>(p.out)[row0 + i] = 0.0f;
+        else reinterpret_cast<uint16_t*>(p.out)[row0 + i] = 0;
       }
     }
-    return;
-  }
-  const int tok_end = min(L, tok0 + p.partition);
-  const int n_pages = (tok_end - tok0 + 15) >> 4;
-  const int pg0 = tok0 >> 4;
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
-  const int n_rounds = (n_pages + CH - 1) / CH;
+  };
+  make_window(B <= 64);
 
-  // ---- the query operand and the scales, loaded before any DMA is in flight (a
-  //      wait on a later load would also wait for every DMA issued before it) ----
-  // ---- query operand: head c (zero if c >= g), in the k order of the K operand ----
-  u32x4 qop[NS];
-  // integer path: q = sq * (q2 + q1 / 128 + q0 / 16384), three int8 digits and a
+  // ---- per-wave constants: logit and output scales ----
+  float kfac = p.sm_log2;
+  if constexpr (KT == DT_INT8 || KT == DT_E4M3 || KT == DT_E5M2) {
+    if (p.k_scale) kfac *= p.k_scale[p.k_scale_per_head ? kvh : 0];
+  }
+  float vfac = 1.0f;
+  if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
+    if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
+  }
+  int koff[KP::NINSTR], voff[VP::NINSTR];
+#pragma unroll
+  for (int t = 0; t < KP::NINSTR; ++t) koff[t] = KP::src(t, lane);
+#pragma unroll
+  for (int t = 0; t < VP::NINSTR; ++t) voff[t] = VP::src(t, lane);
+  const size_t head_pages = (size_t)p.Hkv;     // pages of one block: one per KV head
+  const int q_bytes = g * D * 2;
+
+  // ---- cursor over the rounds of the chunk (wave-uniform) ----
+  int cj = -1, cpg = 0, clo = 0, chi = 0, cqb = kQBuf;
+  int bad = 0;                                 // pages with an out-of-range block id
+  auto next = [&]() {
+    Desc<CH> d;
+    d.b = d.pg = d.L = d.info = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) d.bid[i] = -1;
+    while (cpg >= chi) {                       // on to the next non-empty segment
+      ++cj;
+      if (cj >= nwin) {
+        if (!more) return d;
+        ex_bs = __builtin_amdgcn_readlane(wex, 63) + __builtin_amdgcn_readlane(wnp, 63);
+        bs += 64;
+        make_window(false);
+        cj = 0;
+        if (nwin == 0) return d;
+      }
+      clo = __builtin_amdgcn_readlane(wlo, cj);
+      chi = __builtin_amdgcn_readlane(whi, cj);
+      cpg = clo;
+      if (chi > clo) cqb ^= kQBuf;
+    }
+    const int pages = __builtin_amdgcn_readlane(wnp, cj);
+    const int np = min(CH, chi - cpg);
+    d.b = bs + cj;
+    d.pg = cpg;
+    d.L = __builtin_amdgcn_readlane(wL, cj);
+    d.info = np | cqb | (cpg == clo ? kFirst : 0) | (cpg + CH >= chi ? kLast : 0) |
+             (cpg + np == pages ? kTail : 0) | (clo == 0 && chi == pages ? kWhole : 0);
+    // block ids are scalar loads (the table is read-only here), counted by
+    // lgkmcnt and never by the vmcnt the ring waits on; they are issued two
+    // rounds before the round's DMA
+    const_i32_t* row = (const_i32_t*)(p.block_tables + (size_t)d.b * p.max_blocks_per_seq);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int bb = row[cpg + min(i, np - 1)];
+      const bool inb = (bb >= 0) && (bb < p.num_blocks);
+      if (i < np) {
+        d.bid[i] = inb ? bb : -1;
+        if (!inb) bad++;
+      }
+    }
+    cpg += CH;
+    return d;
+  };
+
+  // DMA of one round into a stage: first the query rows when the round opens a
+  // segment, then K, V (and INT4 metadata) of its pages.  The ring waits count
+  // only the page loads: loads issued before them are older, so a wait that
+  // leaves the newest LPR loads in flight has finished them too.
+  auto issue = [&](const Desc<CH>& d, auto s_tag) {
+    uint8_t* sb = stage_ptr(s_tag);
+    if (d.info & kFirst) {
+      const auto rq = page_rsrc(p.q + ((size_t)d.b * p.Hq + (size_t)kvh * g) * D, q_bytes);
+      uint8_t* qd = qlds + ((d.info & kQBuf) ? p.q_slot : 0);
+      for (int t = 0; t < p.q_slot; t += 1024) dma16(rq, qd + t, t + 16 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const bool ok = d.bid[i] >= 0;
+      const size_t pidx = (size_t)(ok ? d.bid[i] : 0) * head_pages + kvh;
+      const auto rk = page_rsrc(p.k_pages + pidx * KPAGE, ok ? KPAGE : 0);
+#pragma unroll
+      for (int t = 0; t < KP::NINSTR; ++t) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
+      const auto rv = page_rsrc(p.v_pages + pidx * VPAGE, ok ? VPAGE : 0);
+#pragma unroll
+      for (int t = 0; t < VP::NINSTR; ++t) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
+      if constexpr (SG::META) {
+        const auto rkm = page_rsrc(p.k_meta + pidx * 32, ok ? 128 : 0);
+        dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
+        const auto rvm = page_rsrc(p.v_meta + pidx * 32, ok ? 128 : 0);
+        dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
+      }
+    }
+  };
+
+  // ---- segment state ----
+  // query operand: head c (zero if c >= g), in the k order of the K operand.
+  // Integer path: q = sq * (q2 + q1 / 128 + q0 / 16384), three int8 digits and a
   // per-head scale sq = max|q| / 127; each digit's remainder lies in [-64, 64], so
   // no digit clips, and the representation error is below 2^-15 sq per element
+  u32x4 qop[KI8 ? 1 : NS];
   u32x4 qd[KI8 ? 3 : 1][KI8 ? NSI : 1];
-  float sq = 1.0f;
   float qsum_i = 0.0f;   // INT4: sum over d of (16384 q2 + 128 q1 + q0) for head c
-  {
+  float kq = 0.0f;       // integer path: logit = kq * (16384 a2 + 128 a1 + a0)
+  float kq4 = 0.0f;      // INT4: the same times the token's scale
+  float m_ref = -INFINITY;   // exponent reference of head c (uniform over qg)
+  float l_run = 0.0f;        // per-lane partial softmax sum
+  float corr_run = 0.0f;     // INT4 V: per-lane partial of sum (p s) zp
+  f32x4 oacc[NE];
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};   // V_FOLD: sum_t p_t per head (all columns alike)
+
+  auto begin_segment = [&](const Desc<CH>& d) {
+    m_ref = -INFINITY;
+    l_run = 0.0f;
+    corr_run = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sacc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool hv = c < g;
-    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * g + (hv ? c : 0)) * D;
+    const uint32_t qb = lds_addr(qlds + ((d.info & kQBuf) ? p.q_slot : 0)) + (uint32_t)((hv ? c : 0) * D * 2);
+    static_assert(q_runs_ok<KT, D, KI8>(), "query runs");
     if constexpr (KI8) {
-      float qv[NSI][16];
+      // step s2: 16 bf16 values, two 16-byte reads
+      u32x4 raw[NSI][2];
+#pragma unroll
+      for (int s2 = 0; s2 < NSI; ++s2) {
+        const uint32_t a = qb + 2 * q_dim<KT, D, true>(qg, s2, 0);
+        raw[s2][0] = ds_b128(a);
+        raw[s2][1] = ds_b128(a + 16);
+      }
+      lds_fence();
+#pragma unroll
+      for (int s2 = 0; s2 < NSI; ++s2) {
+        lds_tie(raw[s2][0]);
+        lds_tie(raw[s2][1]);
+      }
+      auto qval = [&](int s2, int e) {
+        const int pos = q_dim<KT, D, true>(0, s2, e) - q_dim<KT, D, true>(0, s2, 0);
+        const uint32_t wd = raw[s2][pos >> 3][(pos >> 1) & 3];
+        const float v = __uint_as_float((pos & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        return hv ? v : 0.0f;
+      };
       float amax = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < NSI; ++s2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          qv[s2][e] = bf16_bits_to_f32(qrow[k_dim_i8<KT, D>(qg, s2, e)]);
-          if (!hv) qv[s2][e] = 0.0f;
-          amax = fmaxf(amax, fabsf(qv[s2][e]));
-        }
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(qval(s2, e)));
       amax = fmaxf(amax, shfl_xor_f(amax, 16));
       amax = fmaxf(amax, shfl_xor_f(amax, 32));
-      sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
+      const float sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
       const float inv = 1.0f / sq;
       int dsum[3] = {0, 0, 0};
 #pragma unroll
       for (int s2 = 0; s2 < NSI; ++s2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t w[3] = {0u, 0u, 0u};
+          uint32_t wd[3] = {0u, 0u, 0u};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            float x = fminf(fmaxf(qv[s2][4 * i + k] * inv, -127.0f), 127.0f);
+            float x = fminf(fmaxf(qval(s2, 4 * i + k) * inv, -127.0f), 127.0f);
 #pragma unroll
             for (int dg = 0; dg < 3; ++dg) {
               const float digit = rintf(x);
               x = (x - digit) * 128.0f;
-              w[dg] |= ((uint32_t)(int32_t)digit & 0xffu) << (8 * k);
+              wd[dg] |= ((uint32_t)(int32_t)digit & 0xffu) << (8 * k);
               dsum[dg] += (int)digit;
             }
           }
 #pragma unroll
-          for (int dg = 0; dg < 3; ++dg) qd[dg][s2][i] = w[dg];
+          for (int dg = 0; dg < 3; ++dg) qd[dg][s2][i] = wd[dg];
         }
       }
       if constexpr (KT == DT_INT4) {
@@ -689,103 +909,42 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         }
         qsum_i = (float)(dsum[0] * 128 + dsum[1]) * 128.0f + (float)dsum[2];
       }
+      kq = kfac * sq * (1.0f / 16384.0f);
+      kq4 = p.sm_log2 * sq * (1.0f / 16384.0f);
     } else {
+      // step s: 8 bf16 values, one 16-byte read
+      u32x4 raw[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        uint32_t qb[8];
+      for (int s2 = 0; s2 < NS; ++s2) raw[s2] = ds_b128(qb + 2 * q_dim<KT, D, false>(qg, s2, 0));
+      lds_fence();
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        lds_tie(raw[s2]);
+        uint32_t qb8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qb[e] = (uint32_t)qrow[k_dim<KT, D>(qg, s, e)];
-          if (!hv) qb[e] = 0u;
+          const int pos = q_dim<KT, D, false>(0, s2, e) - q_dim<KT, D, false>(0, s2, 0);
+          const uint32_t wd = raw[s2][pos >> 1];
+          qb8[e] = hv ? ((pos & 1) ? (wd >> 16) : (wd & 0xffffu)) : 0u;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (KBF) {
-            qop[s][i] = qb[2 * i] | (qb[2 * i + 1] << 16);
+            qop[s2][i] = qb8[2 * i] | (qb8[2 * i + 1] << 16);
           } else {
-            f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(qb[2 * i]),
-                                                                            bf16_bits_to_f32(qb[2 * i + 1])));
-            qop[s][i] = __builtin_bit_cast(uint32_t, h2);
+            f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(qb8[2 * i]),
+                                                                            bf16_bits_to_f32(qb8[2 * i + 1])));
+            qop[s2][i] = __builtin_bit_cast(uint32_t, h2);
           }
         }
       }
     }
-  }
-
-  float kfac = p.sm_log2;
-  if constexpr (KT == DT_INT8 || KT == DT_E4M3 || KT == DT_E5M2) {
-    if (p.k_scale) kfac *= p.k_scale[p.k_scale_per_head ? kvh : 0];
-  }
-  // integer path: logit = kfac * sq / 16384 * (16384 a2 + 128 a1 + a0)
-  const float kq = kfac * sq * (1.0f / 16384.0f);
-  const float kq4 = p.sm_log2 * sq * (1.0f / 16384.0f);   // INT4: times the token's scale
-  float vfac = 1.0f;
-  if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
-    if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
-  }
-
-  // ---- block ids of the first rounds and their DMA, then the ring ----
-  // block ids are scalar loads (the table is read-only here), counted by lgkmcnt
-  // and never by the vmcnt the ring waits on
-  const_i32_t* cbt = (const_i32_t*)(bt + pg0);
-  int bad = 0;                                 // pages with an out-of-range block id
-  Round<CH> rd[NST];
-  int koff[KP::NINSTR], voff[VP::NINSTR];
-#pragma unroll
-  for (int t = 0; t < KP::NINSTR; ++t) koff[t] = KP::src(t, lane);
-#pragma unroll
-  for (int t = 0; t < VP::NINSTR; ++t) voff[t] = VP::src(t, lane);
-  const size_t head_pages = (size_t)p.Hkv;     // pages of one block: one per KV head
-
-  auto issue = [&](const Round<CH>& r, auto s_tag) {
-    uint8_t* sb = stage_ptr(s_tag);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const size_t pidx = (size_t)r.bid[i] * head_pages + kvh;
-      const auto rk = page_rsrc(p.k_pages + pidx * KPAGE, r.ok[i] ? KPAGE : 0);
-#pragma unroll
-      for (int t = 0; t < KP::NINSTR; ++t) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
-      const auto rv = page_rsrc(p.v_pages + pidx * VPAGE, r.ok[i] ? VPAGE : 0);
-#pragma unroll
-      for (int t = 0; t < VP::NINSTR; ++t) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
-      if constexpr (SG::META) {
-        const auto rkm = page_rsrc(p.k_meta + pidx * 32, r.ok[i] ? 128 : 0);
-        dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
-        const auto rvm = page_rsrc(p.v_meta + pidx * 32, r.ok[i] ? 128 : 0);
-        dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
-      }
-    }
   };
-  auto fetch = [&](int first) {
-    Round<CH> r;
-    r.np = min(CH, n_pages - first);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int bb = cbt[min(first + i, n_pages - 1)];
-      const bool inb = (bb >= 0) && (bb < p.num_blocks);
-      r.ok[i] = (i < r.np) && inb;
-      r.bid[i] = r.ok[i] ? bb : 0;
-      if (i < r.np && !inb) bad++;
-    }
-    return r;
-  };
-  if (0 < n_rounds) { rd[0] = fetch(0); issue(rd[0], std::integral_constant<int, 0>{}); }
-  if (NST > 2 && 1 < n_rounds) { rd[1] = fetch(CH); issue(rd[1], std::integral_constant<int, 1>{}); }
-  if (NST > 3 && 2 < n_rounds) { rd[2] = fetch(2 * CH); issue(rd[2], std::integral_constant<int, 2>{}); }
 
-  // ---- wave state ----
-  float m_ref = -INFINITY;   // exponent reference of head c (uniform over qg)
-  float l_run = 0.0f;        // per-lane partial softmax sum
-  float corr_run = 0.0f;     // INT4 V: per-lane partial of sum (p s) zp
-  f32x4 oacc[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};   // V_FOLD: sum_t p_t per head (all columns alike)
-
-  // ---- one round from LDS stage `stage`: QK, softmax, PV ----
-  // TAIL: the partition's last round, the only one with pages past the end or a
-  // partial page; full rounds skip every per-token test.
-  auto round = [&](auto tail_tag, const Round<CH>& cur, auto s_tag, int first) {
+  // ---- one round from an LDS stage: QK, softmax, PV ----
+  // TAIL: the round holds the sequence's last page, the only one with tokens past
+  // its end; other rounds skip every per-token test.
+  auto round = [&](auto tail_tag, const Desc<CH>& cur, auto s_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const uint8_t* sb = stage_ptr(s_tag);
 
@@ -847,7 +1006,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2) acc = mfma_qk<KBF>(k_operand<KT, D>(kw, s2), qop[s2], acc);
       }
-      const int tbase = tok0 + (first + i) * 16 + 4 * qg;
+      const int tbase = (cur.pg + i) * 16 + 4 * qg;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float z;
@@ -860,8 +1019,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         } else {
           z = acc[r] * kfac;
         }
-        bool valid = cur.ok[i];
-        if constexpr (TAIL) valid = valid && (tbase + r < tok_end);
+        bool valid = cur.bid[i] >= 0;
+        if constexpr (TAIL) valid = valid && (tbase + r < cur.L);
         z = valid ? z : -INFINITY;
         sl[i][r] = z;
         cmax = fmaxf(cmax, z);
@@ -974,9 +1133,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         v_operands<VT, D>(vw, vop[h2]);
         if constexpr (TAIL && V_NAN) {
           // tokens past the end of the sequence: their slots may hold NaN codes
-          const int tb = tok0 + (first + pi) * 16 + 4 * qg;
-          const uint32_t m01 = ((tb + 0 < tok_end) ? 0x0000ffffu : 0u) | ((tb + 1 < tok_end) ? 0xffff0000u : 0u);
-          const uint32_t m23 = ((tb + 2 < tok_end) ? 0x0000ffffu : 0u) | ((tb + 3 < tok_end) ? 0xffff0000u : 0u);
+          const int tb = (cur.pg + pi) * 16 + 4 * qg;
+          const uint32_t m01 = ((tb + 0 < cur.L) ? 0x0000ffffu : 0u) | ((tb + 1 < cur.L) ? 0xffff0000u : 0u);
+          const uint32_t m23 = ((tb + 2 < cur.L) ? 0x0000ffffu : 0u) | ((tb + 3 < cur.L) ? 0xffff0000u : 0u);
 #pragma unroll
           for (int e = 0; e < NE; ++e) {
             vop[h2][e][0] &= m01;
@@ -997,101 +1156,116 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
     }
   };
 
-  // ---- the rounds: issue round r+NST-1, wait for round r, compute round r; the loop
-  //      is unrolled by NST so that every stage index is a constant ----
-  auto step = [&](auto s_tag, int r) {
-    constexpr int S = decltype(s_tag)::value;
-    constexpr int SA = (S + NST - 1) % NST;          // stage of round r + NST - 1
-    if (r + NST - 1 < n_rounds) {
-      rd[SA] = fetch((r + NST - 1) * CH);
-      issue(rd[SA], std::integral_constant<int, SA>{});
+  // ---- end of a segment: the sequence's output, or the piece's partial ----
+  auto end_segment = [&](const Desc<CH>& d) {
+    float l_all = l_run + shfl_xor_f(l_run, 16);
+    l_all += shfl_xor_f(l_all, 32);
+    float c_all = 0.0f;
+    if constexpr (VT == DT_INT4) {
+      c_all = corr_run + shfl_xor_f(corr_run, 16);
+      c_all += shfl_xor_f(c_all, 32);
     }
-    wait_rounds_after<SG::LPR, NST>(min(NST - 1, n_rounds - 1 - r));
-    if (r + 1 < n_rounds) round(std::false_type{}, rd[S], s_tag, r * CH);
-    else round(std::true_type{}, rd[S], s_tag, r * CH);
-  };
-  for (int r = 0; r < n_rounds; r += NST) {
-    step(std::integral_constant<int, 0>{}, r);
-    if (r + 1 < n_rounds) step(std::integral_constant<int, 1>{}, r + 1);
-    if constexpr (NST > 2) if (r + 2 < n_rounds) step(std::integral_constant<int, 2 % NST>{}, r + 2);
-    if constexpr (NST > 3) if (r + 3 < n_rounds) step(std::integral_constant<int, 3 % NST>{}, r + 3);
-  }
-  if (bad && p.err && lane == 0) atomicAdd(p.err, bad);
-
-  // ---- full softmax sums over the lane groups ----
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
-  if constexpr (VT == DT_INT4) {
-    corr_run += shfl_xor_f(corr_run, 16);
-    corr_run += shfl_xor_f(corr_run, 32);
-  }
-
-  // lane (qg, c) holds O[head 4qg+r][d = NE*c + e]; fetch that head's sums
-  float lh[4], ch[4], mh[4];
+    // lane (qg, c) holds O[head 4qg+r][d = NE*c + e]; fetch that head's sums
+    float lh[4], ch[4], mh[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lh[r] = shfl_f(l_run, 4 * qg + r);
-    ch[r] = shfl_f(corr_run, 4 * qg + r);
-    mh[r] = shfl_f(m_ref, 4 * qg + r);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * qg + r;
-    if (h >= g) continue;
-    const size_t row = (size_t)b * p.Hq + (size_t)kvh * g + h;
-    float o[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float v = oacc[e][r] - ch[r];
-      if constexpr (V_FOLD) v -= V_OFFSET * sacc[r];
-      o[e] = v * vfac;
+    for (int r = 0; r < 4; ++r) {
+      lh[r] = shfl_f(l_all, 4 * qg + r);
+      ch[r] = shfl_f(c_all, 4 * qg + r);
+      mh[r] = shfl_f(m_ref, 4 * qg + r);
     }
-    if (single) {
+    const int slot = w + d.b;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) o[e] = o[e] / lh[r];
-      if (p.out_f32) {
-        float* dst = reinterpret_cast<float*>(p.out) + row * D + NE * c;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * qg + r;
+      if (h >= g) continue;
+      const size_t hq = (size_t)kvh * g + h;
+      float o[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        float v = oacc[e][r] - ch[r];
+        if constexpr (V_FOLD) v -= V_OFFSET * sacc[r];
+        o[e] = v * vfac;
+      }
+      if (d.info & kWhole) {
+        const size_t row = (size_t)d.b * p.Hq + hq;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[e] = (lh[r] > 0.0f) ? o[e] / lh[r] : 0.0f;
+        if (p.out_f32) {
+          float* dst = reinterpret_cast<float*>(p.out) + row * D + NE * c;
+#pragma unroll
+          for (int e = 0; e < NE; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+        } else {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + NE * c;
+          uint32_t pk[NE / 2];
+#pragma unroll
+          for (int e = 0; e < NE; e += 2) pk[e / 2] = (uint32_t)f32_to_bf16_bits(o[e]) | ((uint32_t)f32_to_bf16_bits(o[e + 1]) << 16);
+          if constexpr (NE == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+        }
+      } else {
+        const size_t prow = (size_t)slot * p.Hq + hq;
+        float* dst = p.ws_o + prow * D + NE * c;
 #pragma unroll
         for (int e = 0; e < NE; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-      } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + NE * c;
-        uint32_t pk[NE / 2];
-#pragma unroll
-        for (int e = 0; e < NE; e += 2) pk[e / 2] = (uint32_t)f32_to_bf16_bits(o[e]) | ((uint32_t)f32_to_bf16_bits(o[e + 1]) << 16);
-        if constexpr (NE == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
-      }
-    } else {
-      float* dst = p.ws_o + (row * p.num_partitions + part) * D + NE * c;
-#pragma unroll
-      for (int e = 0; e < NE; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-      if (c == 0) {
-        p.ws_m[row * p.num_partitions + part] = mh[r];
-        p.ws_l[row * p.num_partitions + part] = lh[r];
+        if (c == 0) {
+          p.ws_m[prow] = mh[r];
+          p.ws_l[prow] = lh[r];
+        }
       }
     }
+  };
+
+  auto compute = [&](const Desc<CH>& d, auto s_tag) {
+    if (d.info & kFirst) begin_segment(d);
+    if (d.info & kTail) round(std::true_type{}, d, s_tag);
+    else round(std::false_type{}, d, s_tag);
+    if (d.info & kLast) end_segment(d);
+  };
+
+  // ---- the ring: round r sits in stage r % 2; while it is computed, round r+1
+  //      is in flight and the block ids of round r+2 are being loaded ----
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  Desc<CH> da = next();
+  if (da.info & kNp) {
+    Desc<CH> dn = next();
+    Desc<CH> db;
+    issue(da, S0{});
+    while (true) {
+      if (dn.info & kNp) issue(dn, S1{});
+      db = dn;
+      dn = next();
+      if (db.info & kNp) wait_vmcnt<SG::LPR>();
+      else wait_vmcnt<0>();
+      compute(da, S0{});
+      if (!(db.info & kNp)) break;
+
+      if (dn.info & kNp) issue(dn, S0{});
+      da = dn;
+      dn = next();
+      if (da.info & kNp) wait_vmcnt<SG::LPR>();
+      else wait_vmcnt<0>();
+      compute(db, S1{});
+      if (!(da.info & kNp)) break;
+    }
   }
+  if (bad && p.err && lane == 0) atomicAdd(p.err, bad);
 }
 
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 
-// pages per round and rounds in the LDS ring (the ring holds NST-1 rounds in
-// flight while one is consumed)
+// pages per round (the ring has two stages: one round in flight while one is consumed)
 template <int KT, int VT>
 constexpr int pages_per_round() {
-  return 2;
-}
-template <int KT, int VT>
-constexpr int ring_stages() {
   return 2;
 }
 
 template <int KT, int VT, int D>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, D, pages_per_round<KT, VT>(), ring_stages<KT, VT>()>), grid,
-                     dim3(64), 0, s, prm);
+  hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, pages_per_round<KT, VT>()>), grid, dim3(64),
+                     2 * prm.q_slot, s, prm);
   return hipGetLastError();
 }
 
@@ -1151,19 +1325,23 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   prm.g = a.num_q_heads / c.num_kv_heads;
   prm.max_seq_len = a.max_seq_len;
   prm.sm_log2 = a.softmax_scale * kLog2e;
-  prm.partition = a.partition;
-  prm.num_partitions = a.num_partitions;
+  prm.batch = a.batch;
+  prm.chunk_pages = a.chunk_pages;
+  prm.n_chunks = a.n_chunks;
+  prm.min_chunk = a.min_chunk;
+  prm.q_slot = (prm.g * c.head_dim * 2 + 1023) / 1024 * 1024;
   prm.ws_m = a.ws_m;
   prm.ws_l = a.ws_l;
   prm.ws_o = a.ws_o;
+  prm.ws_rec = reinterpret_cast<int2*>(a.ws_rec);
   prm.out_f32 = a.out_f32;
   prm.out = a.out;
   prm.err = a.err;
 
-  dim3 grid(a.num_partitions, c.num_kv_heads, a.batch);
+  dim3 grid(a.n_chunks, c.num_kv_heads);
   hipError_t e = (c.head_dim == 128) ? launch_kv<128>(c.k_dtype, c.v_dtype, prm, grid, s)
                                      : launch_kv<64>(c.k_dtype, c.v_dtype, prm, grid, s);
-  if (e != hipSuccess || a.num_partitions == 1) return e;
+  if (e != hipSuccess || a.ws_rec == nullptr) return e;
   dim3 rgrid(a.num_q_heads, a.batch);
   if (c.head_dim == 128)
     hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kRedThreads), 0, s, prm);

@@ -11,7 +11,13 @@
 
 namespace {
 
-constexpr int kDefaultPartition = 512;
+// Decode work split: the pages of all sequences, concatenated in sequence order,
+// are cut into chunks; one wave per (chunk, KV head).  Without an explicit
+// partition the chunk count aims at kTargetWaves waves (256 compute units with
+// 8 resident decode waves each) and the device sizes the chunks from the actual
+// page total, never below kMinChunk pages.
+constexpr int64_t kTargetWaves = 2048;
+constexpr int kMinChunk = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -65,23 +71,44 @@ kvq::CacheView view(const kvq_cache* c) {
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-int effective_partition(int32_t partition) { return partition == 0 ? kDefaultPartition : partition; }
+struct Split {
+  int64_t n_chunks;
+  int chunk_pages;   // 0: automatic
+};
 
-// Decode workspace: [m f32 [B][Hq][P]] [l f32 [B][Hq][P]] [acc f32 [B][Hq][P][D]],
-// each region starting on a 16-byte boundary.
+Split decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_seq_len, int32_t partition) {
+  const int64_t bound = batch * ((max_seq_len + 15) / 16);   // pages, at most
+  Split sp;
+  if (partition > 0) {
+    sp.chunk_pages = partition / 16;
+    sp.n_chunks = (bound + sp.chunk_pages - 1) / sp.chunk_pages;
+  } else {
+    sp.chunk_pages = 0;
+    const int64_t target = (kTargetWaves + num_kv_heads - 1) / num_kv_heads;
+    const int64_t most = (bound + kMinChunk - 1) / kMinChunk;
+    sp.n_chunks = target < most ? target : most;
+  }
+  if (sp.n_chunks < 1) sp.n_chunks = 1;
+  return sp;
+}
+
+// Decode workspace, with S = n_chunks + batch piece slots:
+// [m f32 [S][Hq]] [l f32 [S][Hq]] [rec int32 [batch][2]] [acc f32 [S][Hq][D]],
+// each region starting on a 16-byte boundary; none when there is one chunk.
 struct WsLayout {
-  int64_t m, l, o, total;
+  int64_t m, l, rec, o, total;
 };
 
 int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
 
-WsLayout workspace_layout(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t P) {
+WsLayout workspace_layout(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t n_chunks) {
   WsLayout w;
-  const int64_t rows = batch * num_q_heads;
+  const int64_t rows = (n_chunks + batch) * num_q_heads;
   w.m = 0;
-  w.l = w.m + round16(rows * P * 4);
-  w.o = w.l + round16(rows * P * 4);
-  w.total = w.o + rows * P * head_dim * 4;
+  w.l = w.m + round16(rows * 4);
+  w.rec = w.l + round16(rows * 4);
+  w.o = w.rec + round16(batch * 8);
+  w.total = w.o + rows * head_dim * 4;
   return w;
 }
 
@@ -139,13 +166,13 @@ kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const 
                                       static_cast<hipStream_t>(stream)));
 }
 
-size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
-                                 int32_t partition) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition < 0) return 0;
-  const int part = effective_partition(partition);
-  const int64_t P = ((int64_t)max_seq_len + part - 1) / part;
-  if (P <= 1) return 0;
-  return workspace_layout(batch, num_q_heads, head_dim, P).total;
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+  if (partition < 0 || partition % 16 != 0) return 0;
+  const Split sp = decode_split(batch, num_kv_heads, max_seq_len, partition);
+  if (sp.n_chunks <= 1) return 0;
+  return workspace_layout(batch, num_q_heads, head_dim, sp.n_chunks).total;
 }
 
 kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q, const int32_t* block_tables,
@@ -165,10 +192,8 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
   if (!q || !block_tables || !seq_lens || !out) return KVQ_ERR_NULL;
   if (!aligned16(q)) return KVQ_ERR_ALIGN;
   if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_ERR_SHAPE;
-  const int part = effective_partition(partition);
-  const int64_t P64 = max_seq_len > 0 ? ((int64_t)max_seq_len + part - 1) / part : 1;
-  if (P64 > INT32_MAX) return KVQ_ERR_SHAPE;
-  const int P = (int)P64;
+  if ((int64_t)batch * (((int64_t)max_seq_len + 15) / 16) > INT32_MAX / 2) return KVQ_ERR_SHAPE;
+  const Split sp = decode_split(batch, cache->num_kv_heads, max_seq_len, partition);
   kvq::DecodeArgs a;
   a.q = q;
   a.block_tables = block_tables;
@@ -178,18 +203,21 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
   a.max_seq_len = max_seq_len;
   a.num_q_heads = num_q_heads;
   a.softmax_scale = softmax_scale;
-  a.partition = part;
-  a.num_partitions = P;
+  a.chunk_pages = sp.chunk_pages;
+  a.n_chunks = (int)sp.n_chunks;
+  a.min_chunk = kMinChunk;
   a.ws_m = a.ws_l = a.ws_o = nullptr;
-  if (P > 1) {
-    const size_t need = kvq_decode_workspace_size(batch, num_q_heads, cache->head_dim, max_seq_len, partition);
+  a.ws_rec = nullptr;
+  if (sp.n_chunks > 1) {
+    const size_t need = workspace_layout(batch, num_q_heads, cache->head_dim, sp.n_chunks).total;
     if (!workspace) return KVQ_ERR_WORKSPACE;
     if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
-    const WsLayout lay = workspace_layout(batch, num_q_heads, cache->head_dim, P);
+    const WsLayout lay = workspace_layout(batch, num_q_heads, cache->head_dim, sp.n_chunks);
     char* base = static_cast<char*>(workspace);
     a.ws_m = reinterpret_cast<float*>(base + lay.m);
     a.ws_l = reinterpret_cast<float*>(base + lay.l);
+    a.ws_rec = reinterpret_cast<int32_t*>(base + lay.rec);
     a.ws_o = reinterpret_cast<float*>(base + lay.o);
   }
   a.out_f32 = out_dtype == KVQ_F32;

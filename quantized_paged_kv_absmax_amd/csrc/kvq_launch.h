@@ -35,10 +35,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int batch, max_seq_len, num_q_heads;
   float softmax_scale;
-  int partition, num_partitions;
-  float* ws_m;   // [B][Hq][P]
-  float* ws_l;   // [B][Hq][P]
-  float* ws_o;   // [B][Hq][P][D]
+  int chunk_pages;   // pages per chunk, 0: chosen on the device from the total
+  int n_chunks;      // chunks in the launch
+  int min_chunk;     // smallest automatic chunk
+  float* ws_m;       // [slots][Hq]      (all four NULL when n_chunks == 1)
+  float* ws_l;       // [slots][Hq]
+  float* ws_o;       // [slots][Hq][D]
+  int32_t* ws_rec;   // [B][2]
   int out_f32;
   void* out;
   int32_t* err;

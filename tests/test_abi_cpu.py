@@ -79,7 +79,7 @@ def test_decode_argument_errors():
     assert _decode(_cache(), out=None) == _lib.ERR_NULL
     # a split decode needs a workspace of the advertised size
     assert _decode(_cache(), max_seq_len=2000) == _lib.ERR_WORKSPACE
-    need = _lib.load().kvq_decode_workspace_size(2, 4, 128, 2000, 0)
+    need = _lib.load().kvq_decode_workspace_size(2, 4, 2, 128, 2000, 0)
     assert _decode(_cache(), max_seq_len=2000, ws=FAKE, ws_bytes=need - 1) == _lib.ERR_WORKSPACE
     assert _decode(_cache(), max_seq_len=2000, ws=FAKE + 8, ws_bytes=need) == _lib.ERR_ALIGN
     # batch 0 is a no-op that succeeds without touching the device
@@ -88,11 +88,25 @@ def test_decode_argument_errors():
 
 def test_workspace_size():
     lib = _lib.load()
-    assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 0) == 0            # one partition: none
-    assert lib.kvq_decode_workspace_size(4, 32, 128, 512, 256) > 0
-    rows, P, D = 4 * 32, 3, 128                                              # 1100 tokens / 512
     r16 = lambda x: (x + 15) // 16 * 16
-    assert lib.kvq_decode_workspace_size(4, 32, 128, 1100, 0) == 2 * r16(rows * P * 4) + rows * P * D * 4
+
+    def layout(B, Hq, D, n_chunks):
+        rows = (n_chunks + B) * Hq
+        return 2 * r16(rows * 4) + r16(B * 8) + rows * D * 4
+
+    # automatic split: min(ceil(2048 / Hkv), ceil(pages bound / 4)) chunks
+    assert lib.kvq_decode_workspace_size(1, 32, 8, 128, 64, 0) == 0               # 4 pages: one chunk
+    assert lib.kvq_decode_workspace_size(1, 32, 8, 128, 80, 0) == layout(1, 32, 128, 2)
+    assert lib.kvq_decode_workspace_size(64, 32, 8, 128, 4096, 0) == layout(64, 32, 128, 256)
+    assert lib.kvq_decode_workspace_size(64, 32, 3, 128, 4096, 0) == layout(64, 32, 128, 683)
+    # explicit partition: ceil(B * ceil(max_seq_len / 16) / (partition / 16)) chunks
+    assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 512, 512) == layout(4, 32, 128, 4)
+    assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 1100, 256) == layout(4, 32, 128, 18)
+    assert lib.kvq_decode_workspace_size(1, 32, 8, 128, 512, 512) == 0
+    # invalid arguments: 0
+    assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 512, 24) == 0
+    assert lib.kvq_decode_workspace_size(4, 32, 0, 128, 512, 0) == 0
+    assert lib.kvq_decode_workspace_size(0, 32, 8, 128, 512, 0) == 0
 
 
 def test_write_convert_calibrate_argument_errors():

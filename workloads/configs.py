@@ -16,8 +16,7 @@ block_size 16):
   longctx_int8   B=8, lengths U[32768, 131072], Hq=64, Hkv=8, D=128, INT8
                  per-KV-head scales calibrated on 64 synthetic 2048-token
                  sequences; every (K or V, head, channel) has its own standard
-                 deviation drawn once from LogNormal(0, 0.5); 512-token
-                 partitions.
+                 deviation drawn once from LogNormal(0, 0.5).
   int4           B=128, lengths U[1024, 8192], 32/8/128, INT4 asymmetric per
                  (token, KV head); K channels as above, V plain N(0,1); the cache
                  starts as bf16 pages and is converted.
@@ -55,7 +54,7 @@ class Workload:
     calib: str = "prompt"         # prompt | all | set | none
     calib_set: tuple = (0, 0)     # (sequences, tokens each) for calib == "set"
     new_tokens: int = 1           # tokens written by the decode step itself
-    partition: int = 512
+    partition: int = 0            # decode work split: 0 = the library's automatic chunks
     from_bf16_cache: bool = False  # cache starts as bf16 pages, then converted
     block_size: int = BLOCK
 
