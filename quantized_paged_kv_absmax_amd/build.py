@@ -25,6 +25,9 @@ CFLAGS = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax rescale and the integer-logit
+    # combine then touch them without AGPR <-> VGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

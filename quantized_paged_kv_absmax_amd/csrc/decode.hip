@@ -569,12 +569,12 @@ struct Desc {
   int info;       // kNp: pages in the round (0: no round, the chunk is done); flags below
   int bid[CH];    // block id of each page, -1: not loaded (past the segment or out of range)
 };
-constexpr int kNp = 3;           // info bits 0-1
-constexpr int kFirst = 1 << 2;   // first round of its segment
-constexpr int kLast = 1 << 3;    // last round of its segment
-constexpr int kTail = 1 << 4;    // holds the sequence's last page (tokens past L are masked)
-constexpr int kWhole = 1 << 5;   // the segment is the whole sequence
-constexpr int kQBuf = 1 << 6;    // query buffer of the segment (segments alternate)
+constexpr int kNp = 7;           // info bits 0-2
+constexpr int kFirst = 1 << 3;   // first round of its segment
+constexpr int kLast = 1 << 4;    // last round of its segment
+constexpr int kTail = 1 << 5;    // holds the sequence's last page (tokens past L are masked)
+constexpr int kWhole = 1 << 6;   // the segment is the whole sequence
+constexpr int kQBuf = 1 << 7;    // query buffer of the segment (segments alternate)
 
 __device__ __forceinline__ int wave_incl_sum(int v) {
   const int lane = threadIdx.x & 63;
@@ -591,6 +591,7 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 template <int KT, int VT, int D, int CH>
 __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
+  static_assert(CH <= kNp, "pages per round fit the descriptor");
   using KG = Geo<KT, D>;
   using VG = Geo<VT, D>;
   using SG = StageGeo<KT, VT, D, CH>;
@@ -835,15 +836,24 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   float kq = 0.0f;       // integer path: logit = kq * (16384 a2 + 128 a1 + a0)
   float kq4 = 0.0f;      // INT4: the same times the token's scale
   float m_ref = -INFINITY;   // exponent reference of head c (uniform over qg)
-  float l_run = 0.0f;        // per-lane partial softmax sum
   float corr_run = 0.0f;     // INT4 V: per-lane partial of sum (p s) zp
+  float l_run = 0.0f;        // INT4 V: per-lane partial softmax sum (its operand is p s)
   f32x4 oacc[NE];
-  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};   // V_FOLD: sum_t p_t per head (all columns alike)
+  // sum over tokens of the P operand per head (all columns alike), from one MFMA
+  // against a column of ones: the softmax denominator, from the same rounded
+  // weights as the numerator (INT4 V: sum_t p_t s_t, the V offset multiplier),
+  // and (V_FOLD) the multiplier of the V offset
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  // logit factor of this lane's head, 0 for lanes past the group (their logits
+  // become -inf through lane_bias, so their weights are 0)
+  const bool hv_lane = c < g;
+  const float lane_bias = hv_lane ? 0.0f : -INFINITY;
+  float kf_lane = hv_lane ? kfac : 0.0f;
 
   auto begin_segment = [&](const Desc<CH>& d) {
     m_ref = -INFINITY;
-    l_run = 0.0f;
     corr_run = 0.0f;
+    l_run = 0.0f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -909,8 +919,8 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         }
         qsum_i = (float)(dsum[0] * 128 + dsum[1]) * 128.0f + (float)dsum[2];
       }
-      kq = kfac * sq * (1.0f / 16384.0f);
-      kq4 = p.sm_log2 * sq * (1.0f / 16384.0f);
+      kq = hv ? kfac * sq * (1.0f / 16384.0f) : 0.0f;
+      kq4 = hv ? p.sm_log2 * sq * (1.0f / 16384.0f) : 0.0f;
     } else {
       // step s: 8 bf16 values, one 16-byte read
       u32x4 raw[NS];
@@ -1006,44 +1016,49 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2) acc = mfma_qk<KBF>(k_operand<KT, D>(kw, s2), qop[s2], acc);
       }
+      // logit = factor * acc + bias: a page not loaded has factor 0 and bias
+      // -inf, as have lanes past the group, so its weights come out 0
       const int tbase = (cur.pg + i) * 16 + 4 * qg;
+      const bool okp = cur.bid[i] >= 0;
+      const float zb = okp ? lane_bias : -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float z;
         if constexpr (KT == DT_INT4) {
           const float ks = (r < 2) ? ((r == 0) ? km0.x : km0.z) : ((r == 2) ? km1.x : km1.z);
           const float kz = (r < 2) ? ((r == 0) ? km0.y : km0.w) : ((r == 2) ? km1.y : km1.w);
-          z = (ks * kq4) * (acc[r] - kz * qsum_i);
+          z = okp ? fmaf(ks * kq4, acc[r] - kz * qsum_i, lane_bias) : -INFINITY;
         } else if constexpr (KT == DT_INT8) {
-          z = acc[r] * kq;
+          z = fmaf(acc[r], okp ? kq : 0.0f, zb);
         } else {
-          z = acc[r] * kfac;
+          z = fmaf(acc[r], okp ? kf_lane : 0.0f, zb);
         }
-        bool valid = cur.bid[i] >= 0;
-        if constexpr (TAIL) valid = valid && (tbase + r < cur.L);
-        z = valid ? z : -INFINITY;
+        if constexpr (TAIL) z = (tbase + r < cur.L) ? z : -INFINITY;
         sl[i][r] = z;
         cmax = fmaxf(cmax, z);
       }
     }
 
-    // lazy online-softmax update
+    // lazy online-softmax update (the first round of a segment only sets the
+    // reference: its accumulators are still zero)
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-    const bool jump = cmax > m_ref + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(jump)) {
-      const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - cmax) : 1.0f;   // m_ref = -inf -> 0
-      m_ref = jump ? cmax : m_ref;
-      l_run *= alpha;
-      corr_run *= alpha;
-      float ar[4];
+    if (cur.info & kFirst) {
+      m_ref = cmax;
+    } else {
+      const bool jump = cmax > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(jump)) {
+        const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - cmax) : 1.0f;   // m_ref = -inf -> 0
+        m_ref = jump ? cmax : m_ref;
+        corr_run *= alpha;
+        l_run *= alpha;
+        float ar[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = shfl_f(alpha, 4 * qg + r);   // alpha of head 4qg+r
+        for (int r = 0; r < 4; ++r) ar[r] = shfl_f(alpha, 4 * qg + r);   // alpha of head 4qg+r
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
+        for (int e = 0; e < NE; ++e)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[e][r] *= ar[r];
-      if constexpr (V_FOLD) {
+          for (int r = 0; r < 4; ++r) oacc[e][r] *= ar[r];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sacc[r] *= ar[r];
       }
@@ -1063,7 +1078,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pr[r] = __builtin_amdgcn_exp2f(sl[pi][r] - msub);     // -inf -> 0
-          l_run += pr[r];
+          if constexpr (VT == DT_INT4) l_run += pr[r];
         }
         uint32_t a0, a1;
         // V rows 4qg..4qg+3 of the page, this lane's columns (and INT4 metadata)
@@ -1121,13 +1136,11 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
           a0 = pack2(pr[0], pr[1], VBF);
           a1 = pack2(pr[2], pr[3], VBF);
         }
-        aop[2 * h2] = (c < g) ? a0 : 0u;
-        aop[2 * h2 + 1] = (c < g) ? a1 : 0u;
+        aop[2 * h2] = a0;
+        aop[2 * h2 + 1] = a1;
         if constexpr (VBF) {
-          const uint32_t l0 = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
-          const uint32_t l1 = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
-          aop_lo[2 * h2] = (c < g) ? l0 : 0u;
-          aop_lo[2 * h2 + 1] = (c < g) ? l1 : 0u;
+          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
+          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
         }
 
         v_operands<VT, D>(vw, vop[h2]);
@@ -1149,28 +1162,31 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         oacc[e] = mfma_pv2<VBF>(aop, bop, oacc[e]);
         if constexpr (VBF) oacc[e] = mfma_pv2<VBF>(aop_lo, bop, oacc[e]);
       }
-      if constexpr (V_FOLD) {
-        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};   // fp16 1.0
-        sacc = mfma_pv2<false>(aop, ones, sacc);
+      {
+        constexpr uint32_t one2 = VBF ? 0x3F803F80u : 0x3C003C00u;   // bf16 / fp16 1.0 pairs
+        const u32x4 ones = {one2, one2, one2, one2};
+        sacc = mfma_pv2<VBF>(aop, ones, sacc);
+        if constexpr (VBF) sacc = mfma_pv2<VBF>(aop_lo, ones, sacc);
       }
     }
   };
 
   // ---- end of a segment: the sequence's output, or the piece's partial ----
   auto end_segment = [&](const Desc<CH>& d) {
-    float l_all = l_run + shfl_xor_f(l_run, 16);
-    l_all += shfl_xor_f(l_all, 32);
-    float c_all = 0.0f;
+    float c_all = 0.0f, l_all = 0.0f;
     if constexpr (VT == DT_INT4) {
       c_all = corr_run + shfl_xor_f(corr_run, 16);
       c_all += shfl_xor_f(c_all, 32);
+      l_all = l_run + shfl_xor_f(l_run, 16);
+      l_all += shfl_xor_f(l_all, 32);
     }
-    // lane (qg, c) holds O[head 4qg+r][d = NE*c + e]; fetch that head's sums
+    // lane (qg, c) holds O[head 4qg+r][d = NE*c + e] and that head's operand sum;
+    // fetch its reference (and INT4 sums) from the lanes of head 4qg+r
     float lh[4], ch[4], mh[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      lh[r] = shfl_f(l_all, 4 * qg + r);
-      ch[r] = shfl_f(c_all, 4 * qg + r);
+      lh[r] = (VT == DT_INT4) ? shfl_f(l_all, 4 * qg + r) : sacc[r];
+      ch[r] = (VT == DT_INT4) ? shfl_f(c_all, 4 * qg + r) : 0.0f;
       mh[r] = shfl_f(m_ref, 4 * qg + r);
     }
     const int slot = w + d.b;
