@@ -5,8 +5,8 @@
 Headline: the Llama-3-8B-shaped INT8 workload (64 sequences, lengths U[512,
 4096], 32 query / 8 KV heads, head dim 128, per-tensor absmax scales).  One step
 writes the new token of every sequence into the paged cache (kvq_cache_write)
-and runs the paged decode (kvq_paged_attention_decode, 512-token partitions,
-split-KV merge in the same launch).  The page pool is replicated R times
+and runs the paged decode (kvq_paged_attention_decode: balanced chunks of the
+concatenated page list, then the split-KV merge kernel).  The page pool is replicated R times
 (>= 1.5 GB in total) and step s uses copy s % R, so the 256 MB Infinity Cache
 cannot serve the pages from a previous step; inputs are resident in HBM before
 the timed region.
@@ -44,7 +44,78 @@ def parse():
     ap.add_argument("--only", default=None, help="comma list of per-dtype workloads to run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (calibrates HBM byte counters)")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
+                    help="write the text summary of a rocprofv3 --kernel-trace --stats csv run and exit")
+    ap.add_argument("--traffic-summary", nargs=7,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES", "OUT",
+                             "COMMAND"),
+                    help="write HBM bytes per decode call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs "
+                         "of the decode and of the copy probe, and exit")
     return ap.parse_args()
+
+
+def trace_summary(stats_csv, out, command):
+    """Text summary of rocprofv3 kernel statistics (durations in microseconds)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["rocprofv3 kernel-trace summary", "", "command:", "  " + command, "",
+             "kvq_paged_attention_decode source hash: " + decode_source_hash(), "",
+             f"{'kernel':<64} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        name = r["Name"].replace("void ", "").replace("kvq::(anonymous namespace)::", "")
+        name = name.split("(")[0] if "kvq::" in r["Name"] else name[:64]
+        lines.append(f"{name[:64]:<64} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.1f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out, command):
+    """HBM bytes per decode call (chunk + reduce kernels) from FETCH_SIZE / WRITE_SIZE,
+    each scaled by what the same counter reads for a copy of known size."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            d = acc.setdefault(k, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"]) * 1024.0   # KiB
+        return acc
+
+    def avg(acc, key):
+        vals = [v for k, d in acc.items() if key in k for v in d.values()]
+        return (sum(vals) / len(vals), len(vals)) if vals else (0.0, 0)
+
+    copy_bytes = float(copy_bytes)
+    cf, _ = avg(per_kernel(cfetch_csv, "FETCH_SIZE"), "copyBuffer")
+    cw, _ = avg(per_kernel(cwrite_csv, "WRITE_SIZE"), "copyBuffer")
+    if cf == 0.0:
+        cf, _ = avg(per_kernel(cfetch_csv, "FETCH_SIZE"), "")
+        cw, _ = avg(per_kernel(cwrite_csv, "WRITE_SIZE"), "")
+    f_scale, w_scale = copy_bytes / cf, copy_bytes / cw
+    fetch, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    cf_chunk, n = avg(fetch, "decode_chunk_kernel")
+    cf_red, _ = avg(fetch, "decode_reduce_kernel")
+    cw_chunk, _ = avg(wr, "decode_chunk_kernel")
+    cw_red, _ = avg(wr, "decode_reduce_kernel")
+    total = (cf_chunk + cf_red) * f_scale + (cw_chunk + cw_red) * w_scale
+    lines = ["rocprofv3 HBM traffic of one kvq_paged_attention_decode call (llama8b_int8 workload)", "",
+             "command:", "  " + command, "",
+             f"kernel_source_hash: {decode_source_hash()}",
+             f"copy_probe_bytes: {copy_bytes:.0f}",
+             f"fetch_scale (copy bytes / copy FETCH_SIZE bytes): {f_scale:.4f}",
+             f"write_scale (copy bytes / copy WRITE_SIZE bytes): {w_scale:.4f}",
+             f"decode_chunk_kernel dispatches: {n}",
+             f"decode_chunk_kernel fetch_bytes (scaled): {cf_chunk * f_scale:.0f}",
+             f"decode_chunk_kernel write_bytes (scaled): {cw_chunk * w_scale:.0f}",
+             f"decode_reduce_kernel fetch_bytes (scaled): {cf_red * f_scale:.0f}",
+             f"decode_reduce_kernel write_bytes (scaled): {cw_red * w_scale:.0f}",
+             f"hbm_bytes_per_launch: {total:.0f}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def copy_probe(nbytes):
@@ -248,8 +319,9 @@ def time_steps(gw, steps, warmup, with_write=True):
     return total_ms / steps, dec
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle's decode on host cores over a bounded sample of the headline workload."""
+def cpu_baseline(min_s=10.0):
+    """The oracle's decode on host cores over a bounded sample of the headline workload:
+    whole passes over its sequences, one sequence at a time, until min_s of CPU time."""
     import threadpoolctl
     from oracle import attention as oa
     from oracle import cache as oc
@@ -267,14 +339,16 @@ def cpu_baseline(budget_s=12.0):
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     done, nbytes = 0, 0
     t0 = time.perf_counter()
-    while done < w.B and time.perf_counter() - t0 < budget_s:
-        oa.decode(cache, inp.q_bits, inp.block_tables, inp.seq_lens, sm, seqs=[done])
-        nbytes += int(inp.seq_lens[done]) * w.Hkv * 2 * w.D
+    while time.perf_counter() - t0 < min_s:
+        b = done % w.B
+        oa.decode(cache, inp.q_bits, inp.block_tables, inp.seq_lens, sm, seqs=[b])
+        nbytes += int(inp.seq_lens[b]) * w.Hkv * 2 * w.D
         done += 1
     dt = time.perf_counter() - t0
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle fp64 decode of the first {done} of {w.B} sequences of the llama8b_int8 workload "
-                      f"({nbytes / 1e6:.1f} MB of int8 KV, {dt:.1f} s); host os.cpu_count()={os.cpu_count()}"}
+            "sample": f"oracle fp64 decode, one sequence at a time, of {done} sequence decodes "
+                      f"({done / w.B:.2f} passes over the {w.B} sequences of the llama8b_int8 workload; "
+                      f"{nbytes / 1e6:.1f} MB of int8 KV in {dt:.1f} s); host os.cpu_count()={os.cpu_count()}"}
 
 
 def main():
@@ -285,6 +359,12 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
         return
     import torch
     import quantized_paged_kv_absmax_amd as kvq
@@ -346,7 +426,8 @@ def main():
         "config": w,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_partition_kernel<INT8,INT8,128>", "kernel_source_hash": khash},
+                     "kernel": "kvq_paged_attention_decode call: decode_chunk_kernel<INT8,INT8,128> + "
+                               "decode_reduce_kernel<128>", "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "per_dtype": per_dtype,
         "extra": extras,
@@ -358,7 +439,7 @@ WORKLOADS_DESC = {
     "workload": "llama8b_int8: single-layer decode step (write 1 new token per sequence + paged decode), "
                 "Llama-3-8B attention shape, INT8 KV with per-tensor absmax scales",
     "batch": 64, "seq_len": "U[512,4096]", "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
-    "block_size": 16, "partition": 512, "kv_dtype": "int8/int8",
+    "block_size": 16, "work_split": "automatic balanced chunks (partition=0)", "kv_dtype": "int8/int8",
 }
 
 if __name__ == "__main__":

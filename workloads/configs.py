@@ -16,7 +16,8 @@ block_size 16):
   longctx_int8   B=8, lengths U[32768, 131072], Hq=64, Hkv=8, D=128, INT8
                  per-KV-head scales calibrated on 64 synthetic 2048-token
                  sequences; every (K or V, head, channel) has its own standard
-                 deviation drawn once from LogNormal(0, 0.5).
+                 deviation drawn once from LogNormal(0, 0.5); decoded with
+                 512-token work chunks (32 pages) and the merge pass.
   int4           B=128, lengths U[1024, 8192], 32/8/128, INT4 asymmetric per
                  (token, KV head); K channels as above, V plain N(0,1); the cache
                  starts as bf16 pages and is converted.
@@ -84,7 +85,7 @@ WORKLOADS = {
                            k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
     "longctx_int8": Workload("longctx_int8", 4, 8, 64, 8, 128, ("uniform", 32768, 131072),
                              k_gran="per_kv_head", v_gran="per_kv_head", lognormal_sigma=0.5,
-                             calib="set", calib_set=(64, 2048), new_tokens=1),
+                             calib="set", calib_set=(64, 2048), new_tokens=1, partition=512),
     "int4": Workload("int4", 5, 128, 32, 8, 128, ("uniform", 1024, 8192), "int4", "int4",
                      k_gran="per_token_head", v_gran="per_token_head",
                      k_scale_mode="row", v_scale_mode="row",
