@@ -958,46 +958,83 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const uint8_t* sb = stage_ptr(s_tag);
 
+    // every LDS read of the round (K, V and INT4 metadata of its pages) is issued
+    // at once, behind one wait
+    u32x4 kv16[CH][KG::kNPC];
+    u32x2 kv8[CH][KG::kNPC];
+    u32x4 km[CH][2];
+    u32x4 vraw16[CH][4];
+    u32x2 vraw8[CH][4];
+    uint32_t vraw4[CH][4];
+    u32x4 vm[CH][2];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t kb = lds_addr(sb + SG::K_OFF + i * KP::SLOT);
+#pragma unroll
+      for (int j = 0; j < KG::kNPC; ++j) {
+        const uint32_t at = kb + KP::at(c, j * 4 * KG::kPS + qg * KG::kPS);
+        if constexpr (KG::kPS == 16) kv16[i][j] = ds_b128(at);
+        else kv8[i][j] = ds_b64(at);
+      }
+      if constexpr (KT == DT_INT4) {
+        const uint32_t mb = lds_addr(sb + SG::M_OFF + i * 512 + 32 * qg);
+        km[i][0] = ds_b128(mb);
+        km[i][1] = ds_b128(mb + 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t vb = lds_addr(sb + SG::V_OFF + i * VP::SLOT);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t at = vb + VP::at(4 * qg + r, c * VG::kVRowBytes);
+        if constexpr (VG::kVRowBytes == 16) vraw16[i][r] = ds_b128(at);
+        else if constexpr (VG::kVRowBytes == 8) vraw8[i][r] = ds_b64(at);
+        else if constexpr (VG::kVRowBytes == 4) vraw4[i][r] = ds_b32(at);
+        else vraw4[i][r] = ds_u16(at);
+      }
+      if constexpr (VT == DT_INT4) {
+        const uint32_t mb = lds_addr(sb + SG::M_OFF + i * 512 + 256 + 32 * qg);
+        vm[i][0] = ds_b128(mb);
+        vm[i][1] = ds_b128(mb + 16);
+      }
+    }
+    lds_fence();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+#pragma unroll
+      for (int j = 0; j < KG::kNPC; ++j) {
+        if constexpr (KG::kPS == 16) lds_tie(kv16[i][j]);
+        else lds_tie(kv8[i][j]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (VG::kVRowBytes == 16) lds_tie(vraw16[i][r]);
+        else if constexpr (VG::kVRowBytes == 8) lds_tie(vraw8[i][r]);
+        else lds_tie(vraw4[i][r]);
+      }
+      if constexpr (KT == DT_INT4) { lds_tie(km[i][0]); lds_tie(km[i][1]); }
+      if constexpr (VT == DT_INT4) { lds_tie(vm[i][0]); lds_tie(vm[i][1]); }
+    }
+
     // QK: logits of head c for tokens 4qg+r of each page
     float sl[CH][4];
     float cmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const uint32_t kb = lds_addr(sb + SG::K_OFF + i * KP::SLOT);
       uint32_t kw[KG::kKDw];
+#pragma unroll
+      for (int j = 0; j < KG::kNPC; ++j) {
+        if constexpr (KG::kPS == 16) {
+          kw[4 * j] = kv16[i][j][0]; kw[4 * j + 1] = kv16[i][j][1]; kw[4 * j + 2] = kv16[i][j][2]; kw[4 * j + 3] = kv16[i][j][3];
+        } else {
+          kw[2 * j] = kv8[i][j][0]; kw[2 * j + 1] = kv8[i][j][1];
+        }
+      }
       float4 km0, km1;
-      {
-        u32x4 kv16[KG::kNPC];
-        u32x2 kv8[KG::kNPC];
-#pragma unroll
-        for (int j = 0; j < KG::kNPC; ++j) {
-          const uint32_t at = kb + KP::at(c, j * 4 * KG::kPS + qg * KG::kPS);
-          if constexpr (KG::kPS == 16) kv16[j] = ds_b128(at);
-          else kv8[j] = ds_b64(at);
-        }
-        u32x4 m0, m1;
-        if constexpr (KT == DT_INT4) {
-          const uint32_t mb = lds_addr(sb + SG::M_OFF + i * 512 + 32 * qg);
-          m0 = ds_b128(mb);
-          m1 = ds_b128(mb + 16);
-        }
-        lds_fence();
-#pragma unroll
-        for (int j = 0; j < KG::kNPC; ++j) {
-          if constexpr (KG::kPS == 16) {
-            lds_tie(kv16[j]);
-            kw[4 * j] = kv16[j][0]; kw[4 * j + 1] = kv16[j][1]; kw[4 * j + 2] = kv16[j][2]; kw[4 * j + 3] = kv16[j][3];
-          } else {
-            lds_tie(kv8[j]);
-            kw[2 * j] = kv8[j][0]; kw[2 * j + 1] = kv8[j][1];
-          }
-        }
-        if constexpr (KT == DT_INT4) {
-          lds_tie(m0);
-          lds_tie(m1);
-          km0 = __builtin_bit_cast(float4, m0);
-          km1 = __builtin_bit_cast(float4, m1);
-        }
+      if constexpr (KT == DT_INT4) {
+        km0 = __builtin_bit_cast(float4, km[i][0]);
+        km1 = __builtin_bit_cast(float4, km[i][1]);
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (KI8) {
@@ -1082,42 +1119,19 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         }
         uint32_t a0, a1;
         // V rows 4qg..4qg+3 of the page, this lane's columns (and INT4 metadata)
-        const uint32_t vb = lds_addr(sb + SG::V_OFF + pi * VP::SLOT);
         uint32_t vw[4][VG::kVDw];
-        u32x4 vraw16[4];
-        u32x2 vraw8[4];
-        uint32_t vraw4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t at = vb + VP::at(4 * qg + r, c * VG::kVRowBytes);
-          if constexpr (VG::kVRowBytes == 16) vraw16[r] = ds_b128(at);
-          else if constexpr (VG::kVRowBytes == 8) vraw8[r] = ds_b64(at);
-          else if constexpr (VG::kVRowBytes == 4) vraw4[r] = ds_b32(at);
-          else vraw4[r] = ds_u16(at);
-        }
-        u32x4 vm0r, vm1r;
-        if constexpr (VT == DT_INT4) {
-          const uint32_t mb = lds_addr(sb + SG::M_OFF + pi * 512 + 256 + 32 * qg);
-          vm0r = ds_b128(mb);
-          vm1r = ds_b128(mb + 16);
-        }
-        lds_fence();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (VG::kVRowBytes == 16) {
-            lds_tie(vraw16[r]);
-            vw[r][0] = vraw16[r][0]; vw[r][1] = vraw16[r][1]; vw[r][2] = vraw16[r][2]; vw[r][3] = vraw16[r][3];
+            vw[r][0] = vraw16[pi][r][0]; vw[r][1] = vraw16[pi][r][1]; vw[r][2] = vraw16[pi][r][2]; vw[r][3] = vraw16[pi][r][3];
           } else if constexpr (VG::kVRowBytes == 8) {
-            lds_tie(vraw8[r]);
-            vw[r][0] = vraw8[r][0]; vw[r][1] = vraw8[r][1];
+            vw[r][0] = vraw8[pi][r][0]; vw[r][1] = vraw8[pi][r][1];
           } else {
-            lds_tie(vraw4[r]);
-            vw[r][0] = vraw4[r];
+            vw[r][0] = vraw4[pi][r];
           }
         }
+        const u32x4 vm0r = vm[pi][0], vm1r = vm[pi][1];
         if constexpr (VT == DT_INT4) {
-          lds_tie(vm0r);
-          lds_tie(vm1r);
           const float4 vm0 = __builtin_bit_cast(float4, vm0r);
           const float4 vm1 = __builtin_bit_cast(float4, vm1r);
           const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};

@@ -144,6 +144,32 @@ def test_many_short_sequences(kd, vd):
         assert (out[zero] == 0).all()
 
 
+def test_workspace_reused_across_calls():
+    # one workspace through calls with different queries and splits: no piece of
+    # an earlier call may leak into a later one
+    from oracle import attention as oa
+    inp, r, o, ref = _setup("llama8b_int8")
+    w = inp.w
+    need = max(kvq.kvq_decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, inp.max_seq_len, part) for part in (0, 16, 64))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    q_neg = inp.q_bits ^ np.uint16(0x8000)
+    calls = [(64, inp.q_bits), (64, q_neg), (16, inp.q_bits), (0, q_neg), (0, inp.q_bits)]
+    refs = {0: ref, 1: oa.decode(o, q_neg, inp.block_tables, inp.seq_lens, softmax_scale(w.D))}
+    firsts = {}
+    for part, qb in calls:
+        qd = dev_bf16(qb)
+        out = kvq.kvq_paged_attention_decode(r.cache, qd, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                             partition=part, workspace=ws, out_dtype="f32")
+        torch.cuda.synchronize()
+        key = 1 if qb is q_neg else 0
+        mx, nbad = gate_errors(out, refs[key], "f32")
+        log(f"[reuse] partition={part} q={'neg' if key else 'pos'} max|err|={mx:.3e}")
+        assert nbad == 0
+        if (part, key) in firsts:
+            assert torch.equal(out, firsts[(part, key)])
+        firsts[(part, key)] = out
+
+
 def test_bad_block_ids_are_counted_not_faulted():
     w, inp = _small(lens=(40, 33))
     r = build_library_cache(w, inp)
