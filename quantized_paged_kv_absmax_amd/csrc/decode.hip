@@ -63,7 +63,7 @@ struct Params {
   int num_blocks, Hkv, Hq, g;
   int max_seq_len;
   float sm_log2;     // softmax_scale * log2(e)
-  int chunk_pages;   // pages per chunk; 0: ceil(total pages / n_chunks), at least min_chunk, even
+  int chunk_pages;   // pages per chunk; 0: ceil(total pages / n_chunks), at least min_chunk
   int n_chunks;      // chunks in the launch (grid x)
   int min_chunk;
   int q_slot;        // LDS bytes of one query buffer (g * D * 2 rounded up to 1 KB)
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     T += __builtin_amdgcn_readlane(inc, 63);
   }
   int C = p.chunk_pages;
-  if (C == 0) C = (max(p.min_chunk, (T + p.n_chunks - 1) / p.n_chunks) + 1) & ~1;
+  if (C == 0) C = max(p.min_chunk, (T + p.n_chunks - 1) / p.n_chunks);
   const int n_act = max(1, (T + C - 1) / C);
   if (w >= n_act) return;
   const int x0 = w * C, x1 = min(x0 + C, T);
@@ -745,7 +745,15 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   for (int t = 0; t < KP::NINSTR; ++t) koff[t] = KP::src(t, lane);
 #pragma unroll
   for (int t = 0; t < VP::NINSTR; ++t) voff[t] = VP::src(t, lane);
-  const size_t head_pages = (size_t)p.Hkv;     // pages of one block: one per KV head
+  // page addresses: this KV head's first page plus block id times the block
+  // stride (all KV heads of a block), in unsigned 32x32->64 arithmetic
+  const uint8_t* kbase = p.k_pages + (size_t)kvh * KPAGE;
+  const uint8_t* vbase = p.v_pages + (size_t)kvh * VPAGE;
+  const uint32_t kstride = (uint32_t)p.Hkv * KPAGE;
+  const uint32_t vstride = (uint32_t)p.Hkv * VPAGE;
+  const float* kmbase = p.k_meta + (size_t)kvh * 32;
+  const float* vmbase = p.v_meta + (size_t)kvh * 32;
+  const uint32_t mstride = (uint32_t)p.Hkv * 128;
   const int q_bytes = g * D * 2;
 
   // ---- cursor over the rounds of the chunk (wave-uniform) ----
@@ -785,7 +793,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int bb = row[cpg + min(i, np - 1)];
-      const bool inb = (bb >= 0) && (bb < p.num_blocks);
+      const bool inb = (uint32_t)bb < (uint32_t)p.num_blocks;
       if (i < np) {
         d.bid[i] = inb ? bb : -1;
         if (!inb) bad++;
@@ -809,17 +817,20 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const bool ok = d.bid[i] >= 0;
-      const size_t pidx = (size_t)(ok ? d.bid[i] : 0) * head_pages + kvh;
-      const auto rk = page_rsrc(p.k_pages + pidx * KPAGE, ok ? KPAGE : 0);
+      const uint32_t bid = ok ? (uint32_t)d.bid[i] : 0u;
+      const uint64_t koffb = (uint64_t)bid * kstride;
+      const uint64_t voffb = (VPAGE == KPAGE) ? koffb : (uint64_t)bid * vstride;
+      const auto rk = page_rsrc(kbase + koffb, ok ? KPAGE : 0);
 #pragma unroll
       for (int t = 0; t < KP::NINSTR; ++t) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
-      const auto rv = page_rsrc(p.v_pages + pidx * VPAGE, ok ? VPAGE : 0);
+      const auto rv = page_rsrc(vbase + voffb, ok ? VPAGE : 0);
 #pragma unroll
       for (int t = 0; t < VP::NINSTR; ++t) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
       if constexpr (SG::META) {
-        const auto rkm = page_rsrc(p.k_meta + pidx * 32, ok ? 128 : 0);
+        const uint64_t moff = (uint64_t)bid * mstride;
+        const auto rkm = page_rsrc(reinterpret_cast<const uint8_t*>(kmbase) + moff, ok ? 128 : 0);
         dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
-        const auto rvm = page_rsrc(p.v_meta + pidx * 32, ok ? 128 : 0);
+        const auto rvm = page_rsrc(reinterpret_cast<const uint8_t*>(vmbase) + moff, ok ? 128 : 0);
         dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
       }
     }
@@ -1245,7 +1256,23 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     }
   };
 
+  // The two waves sharing a SIMD are served oldest first; left alone, the older
+  // one finishes its chunk long before the younger, and the CU then runs the
+  // rest of the kernel with half its waves.  Each wave lowers its own priority
+  // as its share of the chunk gets done, so the one that is behind is served
+  // first and the waves of a CU finish together.
+  int done_rounds = 0;
+  const int total_rounds = max(1, (x1 - x0 + CH - 1) / CH);
+  auto pace = [&]() {
+    const int q = (4 * done_rounds) / total_rounds;
+    if (q <= 0) __builtin_amdgcn_s_setprio(3);
+    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    ++done_rounds;
+  };
   auto compute = [&](const Desc<CH>& d, auto s_tag) {
+    pace();
     if (d.info & kFirst) begin_segment(d);
     if (d.info & kTail) round(std::true_type{}, d, s_tag);
     else round(std::false_type{}, d, s_tag);
