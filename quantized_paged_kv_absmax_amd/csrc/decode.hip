@@ -2,32 +2,39 @@
 // methods item 3: read the stored codes, convert them to 16-bit, compute; vLLM
 // PR 4893: decode runs a paged-attention kernel), plus the split-KV reduce.
 //
-// Work unit: one wave (a 64-thread workgroup) per (partition, KV head, sequence)
-// serves all g = Hq/Hkv query heads of that KV head, so each K/V page is read from
-// HBM exactly once.  The wave streams its partition CH pages per round with an
-// online softmax; the K pages of round r+1 are loaded while round r's V pages are
-// consumed.  Each page is loaded through a buffer descriptor that spans exactly
+// Work unit: the pages of all sequences, concatenated, are cut into chunks of
+// equal page count; one wave (a 64-thread workgroup) per (chunk, KV head) serves
+// all g = Hq/Hkv query heads of that KV head, so each K/V page is read from HBM
+// exactly once.  A chunk may hold the tail of one sequence and the head of the
+// next (segments); a sequence cut by a chunk boundary leaves partial results
+// that the reduce kernel merges.  The wave streams its chunk CH pages per round
+// with an online softmax, the DMA of round r+1 into LDS overlapping round r's
+// arithmetic.  Each page is loaded through a buffer descriptor that spans exactly
 // that page (0 bytes for a page whose block id is out of range), so the loads
 // need no branches and an invalid page reads as zeros without touching memory.
 //
 // Per page (16 tokens) and wave:
-//   K: lane l loads token l%16, a quarter (l/16) of the row: D/4 elements.  The
-//      codes are turned into exact fp16 (bf16 for a bf16 cache) MFMA operands:
-//        int8  byte ^ 0x80 placed in an fp16 with exponent 2^10, minus 1152
-//        int4  nibble in the same way, minus 1024
-//        e4m3  v_cvt_scalef32_pk_f16_fp8 (scale 1)
-//        e5m2  the byte is the high byte of an fp16
-//      S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_{f16,bf16}, D/32 of them.
-//      Lane l then holds the logits of head l%16 for tokens 4(l/16)+r, r=0..3,
-//      which is exactly the A-operand layout of the 16x16x16 PV product.
+//   K, INT8 / INT4 codes: the codes are the int8 operand of
+//      v_mfma_i32_16x16x64_i8 against the query written as three int8 digits
+//      (INT4 nibbles are unpacked to bytes first).
+//   K, FP8 / BF16: the codes become exact fp16 (bf16) operands (e4m3 through
+//      v_cvt_scalef32_pk_f16_fp8 with scale 1, e5m2 as the high byte of an fp16)
+//      of v_mfma_f32_16x16x32_{f16,bf16} against the query in fp16 (bf16).
+//      Either way lane l then holds the logits of head l%16 for tokens
+//      4(l/16)+r, r=0..3: the A-operand layout of the PV product.
 //   V: lane l loads rows 4(l/16)..4(l/16)+3 at columns [NE*(l%16), NE*(l%16)+NE)
 //      (NE = D/16) and transposes that 4 x NE block in registers with byte
-//      permutes, so that for every column it holds the 4 tokens the B operand of
-//      v_mfma_f32_16x16x16 needs.  NE MFMAs per page accumulate O[head][d].
+//      permutes, so that for every column it holds the 4 tokens the B operand
+//      needs.  Codes become exact 16-bit values (int8: fp16 1152 + code; int4:
+//      bf16 128 + code; fp8 converted to fp16); v_mfma_f32_16x16x32 over two
+//      pages at once accumulates O[head][d], and one more MFMA against a column
+//      of ones gives the sum of the same rounded weights (for the softmax
+//      denominator and to remove the code offsets).
 // Scales: per-tensor / per-head scales multiply the float32 logits (K) and the
 // final output (V).  INT4 uses, per token t with (s_t, zp_t):
 //   logit_t = s_t * (sum_c q_c code_c - zp_t * sum_c q_c)
 //   O       = sum_t (p_t s_t) code_t - sum_t (p_t s_t) zp_t
+// with the weights p_t s_t in bf16 hi + lo (BF16 V splits p_t the same way).
 // Softmax runs in base 2 (log2 e folded into the logit scale).
 // Masking: positions >= seq_len get logit -inf and their V operand is zeroed
 // (an unused slot may hold a NaN code; 0 * NaN would leak).
@@ -255,7 +262,8 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][N], u32x2 (&o
       }
     }
   } else {  // INT4: byte k of a row holds columns 2k (low nibble), 2k+1 (high nibble);
-            // fp16 value 1024 + code, the offset removed after the product
+            // bf16 value 128 + code (exact: 8 significant bits), the offset
+            // removed after the product
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const uint32_t a = vr[2 * pr][0], b = vr[2 * pr + 1][0];
@@ -264,12 +272,12 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][N], u32x2 (&o
         const uint32_t la = hn ? ((a >> 4) & 0x0F0F0F0Fu) : (a & 0x0F0F0F0Fu);
         const uint32_t lb = hn ? ((b >> 4) & 0x0F0F0F0Fu) : (b & 0x0F0F0F0Fu);
         const uint32_t i0 = perm(lb, la, 0x05010400u);   // bytes 0,1 of both rows
-        ob[0 + hn][pr] = perm(kMagic64, i0, kSelLo);     // column 2*0 + hn
-        ob[2 + hn][pr] = perm(kMagic64, i0, kSelHi);     // column 2*1 + hn
+        ob[0 + hn][pr] = perm(kMagic43, i0, kSelLo);     // column 2*0 + hn
+        ob[2 + hn][pr] = perm(kMagic43, i0, kSelHi);     // column 2*1 + hn
         if constexpr (NE == 8) {
           const uint32_t i1 = perm(lb, la, 0x07030602u); // bytes 2,3
-          ob[4 + hn][pr] = perm(kMagic64, i1, kSelLo);
-          ob[6 + hn][pr] = perm(kMagic64, i1, kSelHi);
+          ob[4 + hn][pr] = perm(kMagic43, i1, kSelLo);
+          ob[6 + hn][pr] = perm(kMagic43, i1, kSelHi);
         }
       }
     }
@@ -311,8 +319,13 @@ __device__ __forceinline__ f32x4 mfma_pv2(const u32x4& a, const u32x4& b, const 
   return mfma_qk<BF>(a, b, c);
 }
 
+// two floats -> a packed 16-bit pair, round to nearest even (bf16: one
+// v_cvt_pk_bf16_f32; the weights converted here are never NaN)
 __device__ __forceinline__ uint32_t pack2(float a, float b, bool bf) {
-  if (bf) return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  if (bf) {
+    const bf16x2n v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
   f16x2 v = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
@@ -601,14 +614,18 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   constexpr int NE = VG::kNE;      // PV n-tiles
   constexpr bool KBF = (KT == DT_BF16);
   constexpr bool VBF = (VT == DT_BF16);
+  // PV weights in bf16, split hi + lo (two MFMAs, about 16 significant bits):
+  // BF16 V, and INT4 V, whose weights p_t s_t carry the token's scale and would
+  // leave fp16's range (or its precision) for very large or very small scales
+  constexpr bool WBF = (VT == DT_BF16 || VT == DT_INT4);
   constexpr bool V_NAN = (VT == DT_E4M3 || VT == DT_E5M2 || VT == DT_BF16);  // codes that can decode to NaN/Inf
   constexpr bool KI8 = (KT == DT_INT8 || KT == DT_INT4);   // integer QK path
   constexpr int NSI = D / 64;                               // its k-steps (16 codes each)
-  // V operands carrying a constant offset (fp16 1152 + code, 1024 + code): the
+  // V operands carrying a constant offset (fp16 1152 + code, bf16 128 + code): the
   // offset times sum_t p_t is removed after the product, with sum_t p_t taken from
   // one more MFMA against a column of ones (the same rounded p the product saw)
   constexpr bool V_FOLD = (VT == DT_INT8 || VT == DT_INT4);
-  constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 1024.0f;
+  constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 128.0f;
   constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
 
   // two ring stages, one LDS object each: reads of one stage then carry no
@@ -629,6 +646,19 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   const int B = p.batch;
   const int cap = min(p.max_seq_len, p.max_blocks_per_seq * 16);
   const bool counter = (w == 0 && kvh == 0);   // the one wave that counts clamped lengths
+
+  // warm the caches with the block table: each wave pulls one 256-byte slice of
+  // it (into a ring stage not in use yet), so that the scalar loads of block ids
+  // after the length scan find their lines in L2 or the Infinity Cache
+  {
+    const size_t bt_bytes = (size_t)B * p.max_blocks_per_seq * 4;
+    const size_t off = ((size_t)kvh * gridDim.x + w) * 256;
+    if (off < bt_bytes) {
+      const auto rb = page_rsrc(reinterpret_cast<const uint8_t*>(p.block_tables) + off,
+                                (int)min(bt_bytes - off, (size_t)256));
+      dma4(rb, lds1, 4 * lane);
+    }
+  }
 
   // length of sequence b, clamped to [0, cap] (0 past the batch)
   auto load_len = [&](int b, bool count) {
@@ -1117,7 +1147,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < CH; i += 2) {
       u32x4 aop;
-      u32x4 aop_lo;   // BF16 V: p = p_hi + p_lo, both bf16 (p_hi alone carries only 8 bits)
+      u32x4 aop_lo;   // bf16 weights: w = w_hi + w_lo (w_hi alone carries only 8 bits)
       u32x2 vop[2][NE];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -1150,11 +1180,15 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
           float ps[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ps[r] = (pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
-          a0 = pack2(ps[0], ps[1], false);
-          a1 = pack2(ps[2], ps[3], false);
-          // the correction uses the rounded operand values the MFMA sees
-          const float r0 = unpack_lo(a0, false), r1 = unpack_hi(a0, false);
-          const float r2 = unpack_lo(a1, false), r3 = unpack_hi(a1, false);
+          a0 = pack2(ps[0], ps[1], true);
+          a1 = pack2(ps[2], ps[3], true);
+          const uint32_t b0 = pack2(ps[0] - unpack_lo(a0, true), ps[1] - unpack_hi(a0, true), true);
+          const uint32_t b1 = pack2(ps[2] - unpack_lo(a1, true), ps[3] - unpack_hi(a1, true), true);
+          aop_lo[2 * h2] = b0;
+          aop_lo[2 * h2 + 1] = b1;
+          // the correction uses the operand values the MFMAs see (hi + lo)
+          const float r0 = unpack_lo(a0, true) + unpack_lo(b0, true), r1 = unpack_hi(a0, true) + unpack_hi(b0, true);
+          const float r2 = unpack_lo(a1, true) + unpack_lo(b1, true), r3 = unpack_hi(a1, true) + unpack_hi(b1, true);
           corr_run += (r0 != 0.f ? r0 * vz[0] : 0.f) + (r1 != 0.f ? r1 * vz[1] : 0.f) +
                       (r2 != 0.f ? r2 * vz[2] : 0.f) + (r3 != 0.f ? r3 * vz[3] : 0.f);
         } else {
@@ -1184,14 +1218,14 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
         const u32x4 bop = {vop[0][e][0], vop[0][e][1], vop[1][e][0], vop[1][e][1]};
-        oacc[e] = mfma_pv2<VBF>(aop, bop, oacc[e]);
-        if constexpr (VBF) oacc[e] = mfma_pv2<VBF>(aop_lo, bop, oacc[e]);
+        oacc[e] = mfma_pv2<WBF>(aop, bop, oacc[e]);
+        if constexpr (WBF) oacc[e] = mfma_pv2<WBF>(aop_lo, bop, oacc[e]);
       }
       {
-        constexpr uint32_t one2 = VBF ? 0x3F803F80u : 0x3C003C00u;   // bf16 / fp16 1.0 pairs
+        constexpr uint32_t one2 = WBF ? 0x3F803F80u : 0x3C003C00u;   // bf16 / fp16 1.0 pairs
         const u32x4 ones = {one2, one2, one2, one2};
-        sacc = mfma_pv2<VBF>(aop, ones, sacc);
-        if constexpr (VBF) sacc = mfma_pv2<VBF>(aop_lo, ones, sacc);
+        sacc = mfma_pv2<WBF>(aop, ones, sacc);
+        if constexpr (WBF) sacc = mfma_pv2<WBF>(aop_lo, ones, sacc);
       }
     }
   };

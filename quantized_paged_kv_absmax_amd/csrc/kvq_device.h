@@ -26,6 +26,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -102,6 +103,8 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // halves (1024 + b0, 1024 + b1) from bytes 0,1 (sel 0x04010400) or 2,3 (sel 0x04030402)
 // of x: the byte becomes the low mantissa byte of an fp16 with exponent 2^10.
 constexpr uint32_t kMagic64 = 0x64646464u;
+// the same with bf16 128 (0x4300): halves (128 + b0, 128 + b1), exact for b < 128
+constexpr uint32_t kMagic43 = 0x43434343u;
 constexpr uint32_t kSelLo = 0x04010400u;
 constexpr uint32_t kSelHi = 0x04030402u;
 
