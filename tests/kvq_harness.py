@@ -52,12 +52,12 @@ class LibRun:
     pass
 
 
-def build_library_cache(w, inp, device="cuda"):
+def build_library_cache(w, inp, device="cuda", calib=None):
     r = LibRun()
     c = kvq.PagedKVCache(inp.num_blocks, w.Hkv, w.D, w.k_dtype, w.v_dtype, k_gran=w.k_gran, v_gran=w.v_gran,
                          device=device)
     kt, vt = _scale_plan(w)
-    ck, cv = make_calibration_set(w, inp)
+    ck, cv = make_calibration_set(w, inp) if calib is None else calib
     if kt:
         kvq.kvq_calibrate_scales(dev_bf16(ck, device), w.k_gran, kt, c.k_absmax, c.k_scale)
     if vt:
@@ -117,6 +117,44 @@ def build_oracle_cache(w, inp):
     return c
 
 
+def seq_token_rows(inp, seqs):
+    """Token-major row indices of the given sequences."""
+    return np.concatenate([np.arange(inp.cu[b], inp.cu[b + 1]) for b in seqs]) if len(seqs) else np.zeros(0, np.int64)
+
+
+def build_oracle_cache_sampled(w, inp, seqs, calib=None):
+    """The oracle cache at full pool size holding only the tokens of ``seqs``.
+
+    Scales are calibrated on the workload's whole calibration set, as the
+    library does; only the sampled sequences' rows are encoded (a bf16 source
+    cache is converted block by block over those sequences' blocks).
+    """
+    kt, vt = _scale_plan(w)
+    ck, cv = make_calibration_set(w, inp) if calib is None else calib
+    ks = vs = None
+    kabs = vabs = None
+    if kt:
+        kabs, ks = oc.calibrate(ck, w.k_gran, QMAX[kt])
+    if vt:
+        vabs, vs = oc.calibrate(cv, w.v_gran, QMAX[vt])
+    del ck, cv
+    if w.k_scale_mode == "one" and w.k_dtype in QMAX:
+        ks = np.ones(1, np.float32)
+    if w.v_scale_mode == "one" and w.v_dtype in QMAX:
+        vs = np.ones(1, np.float32)
+    c = oc.PagedCache(inp.num_blocks, w.Hkv, w.D, w.k_dtype, w.v_dtype, k_scale=ks, v_scale=vs)
+    rows = seq_token_rows(inp, seqs)
+    if w.from_bf16_cache:
+        kp = scatter_rows_to_pages(inp.k_bits[rows], inp.slot_mapping[rows], inp.num_blocks)
+        vp = scatter_rows_to_pages(inp.v_bits[rows], inp.slot_mapping[rows], inp.num_blocks)
+        for blk in np.unique(inp.slot_mapping[rows] // 16):
+            c.convert_from_bf16(kp, vp, int(blk), 1)
+    else:
+        c.write(inp.k_bits[rows], inp.v_bits[rows], inp.slot_mapping[rows])
+    c.kabs, c.vabs = kabs, vabs
+    return c
+
+
 # ---------------------------------------------------------------------------
 # comparisons
 # ---------------------------------------------------------------------------
@@ -129,12 +167,29 @@ def valid_slot_mask(inp):
     return m
 
 
-def assert_codes_equal(r, oracle_cache, inp):
-    """Bit-exact comparison of every written slot (codes and INT4 metadata)."""
-    vm = valid_slot_mask(inp)
+def assert_codes_equal(r, oracle_cache, inp, seqs=None):
+    """Bit-exact comparison of every written slot (codes and INT4 metadata), or,
+    with ``seqs``, of the slots of those sequences only."""
+    if seqs is None:
+        vm = valid_slot_mask(inp)
+        blocks = None
+    else:
+        slots = inp.slot_mapping[seq_token_rows(inp, seqs)]
+        blocks = np.unique(slots // 16)
+        pos = np.searchsorted(blocks, slots // 16)
+        vm = np.zeros((blocks.size, 16), bool)
+        vm[pos, slots % 16] = True
+
+    def pick(t, host):
+        if blocks is None:
+            return t.cpu().numpy() if not host else t
+        if host:
+            return t[blocks]
+        return t[torch.from_numpy(blocks).to(t.device)].cpu().numpy()
+
     for which in ("k", "v"):
-        got = getattr(r.cache, which + "_pages").cpu().numpy()
-        ref = getattr(oracle_cache, which + "_pages")
+        got = pick(getattr(r.cache, which + "_pages"), False)
+        ref = pick(getattr(oracle_cache, which + "_pages"), True)
         dt = getattr(oracle_cache, which + "_dtype")
         g = got.transpose(0, 2, 1, 3)[vm]      # [slots][H][rb]
         e = ref.transpose(0, 2, 1, 3)[vm]
@@ -146,8 +201,8 @@ def assert_codes_equal(r, oracle_cache, inp):
             bad = g != e
         assert not bad.any(), f"{which}: {int(bad.sum())} code bytes differ (first at {np.argwhere(bad)[:3].tolist()})"
         if dt == "int4":
-            gm = getattr(r.cache, which + "_meta").cpu().numpy().transpose(0, 2, 1, 3)[vm]
-            em = getattr(oracle_cache, which + "_meta").transpose(0, 2, 1, 3)[vm]
+            gm = pick(getattr(r.cache, which + "_meta"), False).transpose(0, 2, 1, 3)[vm]
+            em = pick(getattr(oracle_cache, which + "_meta"), True).transpose(0, 2, 1, 3)[vm]
             assert np.array_equal(gm.view(np.uint32), em.view(np.uint32)), f"{which} int4 metadata differs"
 
 
@@ -194,5 +249,6 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-__all__ = ["dev_bf16", "build_library_cache", "library_decode", "build_oracle_cache", "assert_codes_equal",
+__all__ = ["dev_bf16", "build_library_cache", "library_decode", "build_oracle_cache", "build_oracle_cache_sampled",
+           "seq_token_rows", "assert_codes_equal",
            "gate_errors", "oracle_decode", "sample_rows", "log", "softmax_scale", "math", "ceil_div"]

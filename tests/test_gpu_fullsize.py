@@ -1,0 +1,107 @@
+"""GPU parity at the measured sizes: every workload the benchmark times, at its
+full batch, lengths and pool, decoded with the same work split (the
+workload's ``partition``) and output type (bf16) as the timed step.
+
+The oracle cannot encode and attend the whole batch in seconds, so it builds
+the same full-size pool holding only a few sampled sequences (scales still
+calibrated on the workload's whole calibration set) and checks:
+  * every code byte (and INT4 scale / zero point) of those sequences'
+    slots, bit-exact, plus the calibrated scales;
+  * the decode output of sampled (sequence, query head) rows — the longest and
+    shortest sequence always among them — within the output tolerance;
+  * that every output row of the whole batch is finite, and that each sampled
+    output, a convex combination of its sequence's dequantised V rows, lies
+    within their per-channel range.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_paged_kv_absmax_amd as kvq
+from tests.kvq_harness import (assert_codes_equal, build_library_cache, build_oracle_cache_sampled, gate_errors,
+                               library_decode, log, oracle_decode, softmax_scale)
+from workloads import WORKLOADS, make_calibration_set, make_decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["llama8b_int8", "fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "bf16", "int4", "longctx_int8"]
+N_SEQS = {"longctx_int8": 2}   # 32K-131K-token sequences: two suffice, four heads each
+N_HEADS = 4
+
+
+def _sample(inp, name, seed):
+    rng = np.random.default_rng(seed)
+    L = inp.seq_lens
+    seqs = {int(np.argmax(L)), int(np.argmin(L))}
+    n = N_SEQS.get(name, 4)
+    rest = [b for b in range(inp.w.B) if b not in seqs]
+    seqs |= set(rng.choice(rest, size=max(0, n - len(seqs)), replace=False).tolist())
+    heads = sorted(rng.choice(inp.w.Hq, size=N_HEADS, replace=False).tolist())
+    g = inp.w.Hq // inp.w.Hkv
+    if 0 not in [h // g for h in heads]:      # KV head 0 holds the merge bookkeeping
+        heads[0] = 0
+    return sorted(seqs), sorted(set(heads))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_codes_and_sampled_decode(name):
+    w = WORKLOADS[name]
+    inp = make_decode_inputs(w)
+    seqs, heads = _sample(inp, name, seed=17)
+    log(f"[{name}] B={w.B} blocks={inp.num_blocks} max_len={inp.max_seq_len} partition={w.partition} "
+        f"seqs={seqs} lens={inp.seq_lens[seqs].tolist()} heads={heads}")
+    calib = make_calibration_set(w, inp)
+    r = build_library_cache(w, inp, calib=calib)
+    assert int(r.err.item()) == 0
+    log(f"[{name}] library cache built; decoding")
+    out = library_decode(r, inp, partition=w.partition, out_dtype="bf16")
+    torch.cuda.synchronize()
+    o = build_oracle_cache_sampled(w, inp, seqs, calib=calib)
+    del calib
+    if o.kabs is not None:
+        assert np.array_equal(r.cache.k_absmax.cpu().numpy(), o.kabs)
+        assert np.array_equal(r.cache.k_scale.cpu().numpy(), o.k_scale)
+    if o.vabs is not None:
+        assert np.array_equal(r.cache.v_absmax.cpu().numpy(), o.vabs)
+        assert np.array_equal(r.cache.v_scale.cpu().numpy(), o.v_scale)
+    assert_codes_equal(r, o, inp, seqs=seqs)
+    log(f"[{name}] codes bit-exact on {len(seqs)} sequences")
+
+    of = out.float()
+    nonempty = torch.from_numpy(inp.seq_lens > 0).to(of.device)
+    assert bool(torch.isfinite(of[nonempty]).all()), "non-finite output row"
+
+    ref = oracle_decode(o, inp, heads=heads, seqs=seqs)
+    got = out[seqs][:, heads]
+    e, bad = gate_errors(got, ref[seqs][:, heads], "bf16")
+    log(f"[{name}] sampled decode max|err| {e:.2e}, violations {bad}")
+    assert bad == 0
+
+    # a convex combination of V rows: each output lies within its sequence's V range
+    g = w.Hq // w.Hkv
+    for i, b in enumerate(seqs):
+        for j, h in enumerate(heads):
+            V = o.gather(inp.block_tables[b], int(inp.seq_lens[b]), "v", [h // g])[:, 0, :].astype(np.float64)
+            lo, hi = V.min(axis=0), V.max(axis=0)
+            x = got[i, j].float().cpu().numpy().astype(np.float64)
+            slack = 4e-3 + np.abs(np.stack([lo, hi])).max(axis=0) * 2.0 ** -8
+            assert np.all(x >= lo - slack) and np.all(x <= hi + slack), (b, h)
+    del r, out
+    torch.cuda.empty_cache()
+
+
+def test_full_size_workspace_matches_bench_layout():
+    """The workspace the benchmark allocates is the size the library asks for,
+    and a decode into a caller-given workspace equals one with its own."""
+    w = WORKLOADS["llama8b_int8"]
+    inp = make_decode_inputs(w, B=16)
+    r = build_library_cache(w, inp)
+    ws_bytes = kvq.kvq_decode_workspace_size(16, w.Hq, w.Hkv, w.D, inp.max_seq_len, 0)
+    ws = torch.full((max(ws_bytes, 16),), 0x7F, dtype=torch.uint8, device="cuda")
+    a = kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                       partition=0, out_dtype="bf16", workspace=ws)
+    b = kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                       partition=0, out_dtype="bf16")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

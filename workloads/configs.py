@@ -29,7 +29,10 @@ benchmarks used trained weights and real prompts; normally distributed
 synthetic values with a few large channels stand in for them here.
 """
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
+import os
+
 import numpy as np
 
 BLOCK = 16
@@ -156,29 +159,48 @@ def _lengths(w, rng):
     return rng.integers(lo, hi, size=w.B, endpoint=True).astype(np.int32)
 
 
-def _normal_bf16(rng, shape, chunk_rows=1 << 16):
-    """N(0,1) float32 draws rounded to bf16, generated in row chunks to bound memory."""
+_CHUNK_ROWS = 1 << 14
+
+
+def _chunked_bf16(rng, shape, chan_scale):
+    """[chan_scale *] N(0,1) float32 draws rounded to bf16, in row chunks.
+
+    Each chunk of _CHUNK_ROWS rows draws from its own PCG64 generator, seeded
+    from ``rng`` in chunk order, so the values do not depend on how many
+    threads fill the chunks (the draws run in parallel; numpy releases the GIL
+    for them).
+    """
     rows = shape[0]
     out = np.empty(shape, np.uint16)
     inner = int(np.prod(shape[1:]))
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0) * inner, dtype=np.float32).reshape((r1 - r0,) + tuple(shape[1:]))
-        out[r0:r1] = f32_to_bf16_bits(x)
+    n_chunks = -(-rows // _CHUNK_ROWS)
+    seeds = rng.integers(0, 2 ** 63, size=n_chunks, dtype=np.int64)
+    cs = None if chan_scale is None else np.asarray(chan_scale, np.float32)
+
+    def fill(k):
+        r0 = k * _CHUNK_ROWS
+        r1 = min(rows, r0 + _CHUNK_ROWS)
+        g = np.random.Generator(np.random.PCG64(int(seeds[k])))
+        x = g.standard_normal((r1 - r0) * inner, dtype=np.float32).reshape((r1 - r0,) + tuple(shape[1:]))
+        out[r0:r1] = f32_to_bf16_bits(x if cs is None else x * cs)
+
+    if n_chunks <= 1:
+        for k in range(n_chunks):
+            fill(k)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, n_chunks)) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out
 
 
-def _scaled_normal_bf16(rng, shape, chan_scale, chunk_rows=1 << 16):
+def _normal_bf16(rng, shape):
+    """N(0,1) float32 draws rounded to bf16."""
+    return _chunked_bf16(rng, shape, None)
+
+
+def _scaled_normal_bf16(rng, shape, chan_scale):
     """chan_scale [Hkv][D] * N(0,1), rounded to bf16 once (the product is the sample)."""
-    rows = shape[0]
-    out = np.empty(shape, np.uint16)
-    inner = int(np.prod(shape[1:]))
-    cs = np.asarray(chan_scale, np.float32)
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0) * inner, dtype=np.float32).reshape((r1 - r0,) + tuple(shape[1:]))
-        out[r0:r1] = f32_to_bf16_bits(x * cs)
-    return out
+    return _chunked_bf16(rng, shape, chan_scale)
 
 
 def _channel_scales(w, streams):
