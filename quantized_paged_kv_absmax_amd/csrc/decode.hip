@@ -320,7 +320,7 @@ __device__ __forceinline__ f32x4 mfma_pv2(const u32x4& a, const u32x4& b, const 
 }
 
 // two floats -> a packed 16-bit pair, round to nearest even (bf16: one
-// v_cvt_pk_bf16_f32; the weights converted here are never NaN)
+// v_cvt_pk_bf16_f32, which turns a NaN into a quiet NaN)
 __device__ __forceinline__ uint32_t pack2(float a, float b, bool bf) {
   if (bf) {
     const bf16x2n v = {(__bf16)a, (__bf16)b};
@@ -397,31 +397,39 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
   constexpr int LPG = D / 4;                  // lanes per group
   constexpr int NG = kRedThreads / LPG;       // groups
   const int hq = blockIdx.x, b = blockIdx.y;
+  // the workspace pointers are read before rec, so that the loads of the pieces
+  // follow rec's load by one memory round trip, not by another kernel-argument one
+  const float* wm = p.ws_m;
+  const float* wl = p.ws_l;
+  const float* wo = p.ws_o;
+  const int Hq = p.Hq;
+  asm volatile("" ::"s"(wm), "s"(wl), "s"(wo), "s"(Hq));
   const int2 rec = p.ws_rec[b];
   if (rec.y <= rec.x) return;                 // one piece: the chunk kernel wrote the row
   const int P = rec.y - rec.x + 1;
   const size_t s0 = (size_t)rec.x + b;
-  const float* m = p.ws_m + s0 * p.Hq + hq;
-  const float* l = p.ws_l + s0 * p.Hq + hq;
-  const float* o = p.ws_o + (s0 * p.Hq + hq) * D;
+  const float* m = wm + s0 * Hq + hq;
+  const float* l = wl + s0 * Hq + hq;
+  const float* o = wo + (s0 * Hq + hq) * D;
 
   const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = grp; j < P; j += NG) {
-    const float mj = m[(size_t)j * p.Hq];
-    if (mj == -INFINITY) continue;            // a piece with no valid token
-    const float lj = l[(size_t)j * p.Hq];
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * p.Hq * D + 4 * ln);
-    if (mj > M) {
-      const float sc = __builtin_amdgcn_exp2f(M - mj);
-      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
-      den *= sc;
-      M = mj;
-    }
-    const float f = __builtin_amdgcn_exp2f(mj - M);
-    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
-    den += f * lj;
+    // branch-free, so the three loads go out together
+    const float mj = m[(size_t)j * Hq];
+    const float lj = l[(size_t)j * Hq];
+    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * Hq * D + 4 * ln);
+    const bool ok = (mj != -INFINITY);        // -inf: a piece with no valid token
+    const float Mn = ok ? fmaxf(M, mj) : M;
+    const float sc = (Mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float f = ok ? __builtin_amdgcn_exp2f(mj - Mn) : 0.0f;
+    acc.x = acc.x * sc + (ok ? f * v.x : 0.0f);
+    acc.y = acc.y * sc + (ok ? f * v.y : 0.0f);
+    acc.z = acc.z * sc + (ok ? f * v.z : 0.0f);
+    acc.w = acc.w * sc + (ok ? f * v.w : 0.0f);
+    den = den * sc + (ok ? f * lj : 0.0f);
+    M = Mn;
   }
   __shared__ float4 s_acc[NG][LPG];
   __shared__ float s_m[NG], s_den[NG];
@@ -916,49 +924,59 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         lds_tie(raw[s2][0]);
         lds_tie(raw[s2][1]);
       }
+      // lanes of a padding head (c >= g) read head 0's row; their digits come out
+      // zero through inv = 0 below
       auto qval = [&](int s2, int e) {
         const int pos = q_dim<KT, D, true>(0, s2, e) - q_dim<KT, D, true>(0, s2, 0);
         const uint32_t wd = raw[s2][pos >> 3][(pos >> 1) & 3];
-        const float v = __uint_as_float((pos & 1) ? (wd & 0xffff0000u) : (wd << 16));
-        return hv ? v : 0.0f;
+        return __uint_as_float((pos & 1) ? (wd & 0xffff0000u) : (wd << 16));
       };
       float amax = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < NSI; ++s2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(qval(s2, e)));
-      amax = fmaxf(amax, shfl_xor_f(amax, 16));
-      amax = fmaxf(amax, shfl_xor_f(amax, 32));
+      amax = xor32_max(xor16_max(amax));
       const float sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
-      const float inv = 1.0f / sq;
-      int dsum[3] = {0, 0, 0};
+      const float inv = hv ? 1.0f / sq : 0.0f;
+      // digits by the 1.5 * 2^23 trick: for |x| < 2^22, x + M rounds x to the
+      // nearest integer (ties to even, as rintf) and holds it, in two's
+      // complement, in its low mantissa bits; (x + M) - M is that integer
+      constexpr float kM = 12582912.0f;
+      float dsum[3] = {0.f, 0.f, 0.f};      // INT4: digit sums (exact small integers)
 #pragma unroll
       for (int s2 = 0; s2 < NSI; ++s2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t wd[3] = {0u, 0u, 0u};
+          uint32_t tb[3][4];                // bits of x + M: the digit in the low byte
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            float x = fminf(fmaxf(qval(s2, 4 * i + k) * inv, -127.0f), 127.0f);
+            // |x| <= 127 up to rounding, so the first digit lies in [-127, 127]
+            float x = qval(s2, 4 * i + k) * inv;
 #pragma unroll
             for (int dg = 0; dg < 3; ++dg) {
-              const float digit = rintf(x);
-              x = (x - digit) * 128.0f;
-              wd[dg] |= ((uint32_t)(int32_t)digit & 0xffu) << (8 * k);
-              dsum[dg] += (int)digit;
+              const float t = x + kM;
+              const float digit = t - kM;
+              tb[dg][k] = __float_as_uint(t);
+              if (dg < 2) x = (x - digit) * 128.0f;
+              if constexpr (KT == DT_INT4) dsum[dg] += digit;
             }
           }
+          // low bytes of the four words: [k0 k1 k2 k3]
 #pragma unroll
-          for (int dg = 0; dg < 3; ++dg) qd[dg][s2][i] = wd[dg];
+          for (int dg = 0; dg < 3; ++dg) {
+            const uint32_t lo = perm(tb[dg][1], tb[dg][0], 0x0c0c0400u);
+            const uint32_t hi = perm(tb[dg][3], tb[dg][2], 0x0c0c0400u);
+            qd[dg][s2][i] = perm(hi, lo, 0x05040100u);
+          }
         }
       }
       if constexpr (KT == DT_INT4) {
 #pragma unroll
         for (int dg = 0; dg < 3; ++dg) {
-          dsum[dg] += __shfl_xor(dsum[dg], 16, 64);
-          dsum[dg] += __shfl_xor(dsum[dg], 32, 64);
+          dsum[dg] = xor32_sum(xor16_sum(dsum[dg]));
         }
-        qsum_i = (float)(dsum[0] * 128 + dsum[1]) * 128.0f + (float)dsum[2];
+        qsum_i = (dsum[0] * 128.0f + dsum[1]) * 128.0f + dsum[2];
       }
       kq = hv ? kfac * sq * (1.0f / 16384.0f) : 0.0f;
       kq4 = hv ? p.sm_log2 * sq * (1.0f / 16384.0f) : 0.0f;
@@ -1119,8 +1137,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 
     // lazy online-softmax update (the first round of a segment only sets the
     // reference: its accumulators are still zero)
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    cmax = xor32_max(xor16_max(cmax));
     if (cur.info & kFirst) {
       m_ref = cmax;
     } else {
@@ -1177,20 +1194,19 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
           const float4 vm1 = __builtin_bit_cast(float4, vm1r);
           const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
           const float vz[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
+          // only the sequence's last page holds unwritten slots, whose metadata
+          // may be NaN: there a zero weight must not meet it
           float ps[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ps[r] = (pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
+          for (int r = 0; r < 4; ++r) ps[r] = (!TAIL || pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
           a0 = pack2(ps[0], ps[1], true);
           a1 = pack2(ps[2], ps[3], true);
-          const uint32_t b0 = pack2(ps[0] - unpack_lo(a0, true), ps[1] - unpack_hi(a0, true), true);
-          const uint32_t b1 = pack2(ps[2] - unpack_lo(a1, true), ps[3] - unpack_hi(a1, true), true);
-          aop_lo[2 * h2] = b0;
-          aop_lo[2 * h2 + 1] = b1;
-          // the correction uses the operand values the MFMAs see (hi + lo)
-          const float r0 = unpack_lo(a0, true) + unpack_lo(b0, true), r1 = unpack_hi(a0, true) + unpack_hi(b0, true);
-          const float r2 = unpack_lo(a1, true) + unpack_lo(b1, true), r3 = unpack_hi(a1, true) + unpack_hi(b1, true);
-          corr_run += (r0 != 0.f ? r0 * vz[0] : 0.f) + (r1 != 0.f ? r1 * vz[1] : 0.f) +
-                      (r2 != 0.f ? r2 * vz[2] : 0.f) + (r3 != 0.f ? r3 * vz[3] : 0.f);
+          aop_lo[2 * h2] = pack2(ps[0] - unpack_lo(a0, true), ps[1] - unpack_hi(a0, true), true);
+          aop_lo[2 * h2 + 1] = pack2(ps[2] - unpack_lo(a1, true), ps[3] - unpack_hi(a1, true), true);
+          // the zero-point term from the unrounded weights (hi + lo equals them to
+          // about 2^-17; this keeps the error off the term zp, which is unbounded)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) corr_run += (!TAIL || ps[r] != 0.0f) ? ps[r] * vz[r] : 0.0f;
         } else {
           a0 = pack2(pr[0], pr[1], VBF);
           a1 = pack2(pr[2], pr[3], VBF);
@@ -1234,10 +1250,8 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   auto end_segment = [&](const Desc<CH>& d) {
     float c_all = 0.0f, l_all = 0.0f;
     if constexpr (VT == DT_INT4) {
-      c_all = corr_run + shfl_xor_f(corr_run, 16);
-      c_all += shfl_xor_f(c_all, 32);
-      l_all = l_run + shfl_xor_f(l_run, 16);
-      l_all += shfl_xor_f(l_all, 32);
+      c_all = xor32_sum(xor16_sum(corr_run));
+      l_all = xor32_sum(xor16_sum(l_run));
     }
     // lane (qg, c) holds O[head 4qg+r][d = NE*c + e] and that head's operand sum;
     // fetch its reference (and INT4 sums) from the lanes of head 4qg+r
@@ -1263,8 +1277,10 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       }
       if (d.info & kWhole) {
         const size_t row = (size_t)d.b * p.Hq + hq;
+        // one reciprocal per row (within an ulp of dividing each element)
+        const float rl = (lh[r] > 0.0f) ? 1.0f / lh[r] : 0.0f;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) o[e] = (lh[r] > 0.0f) ? o[e] / lh[r] : 0.0f;
+        for (int e = 0; e < NE; ++e) o[e] *= rl;
         if (p.out_f32) {
           float* dst = reinterpret_cast<float*>(p.out) + row * D + NE * c;
 #pragma unroll
@@ -1273,7 +1289,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + NE * c;
           uint32_t pk[NE / 2];
 #pragma unroll
-          for (int e = 0; e < NE; e += 2) pk[e / 2] = (uint32_t)f32_to_bf16_bits(o[e]) | ((uint32_t)f32_to_bf16_bits(o[e + 1]) << 16);
+          for (int e = 0; e < NE; e += 2) pk[e / 2] = pack2(o[e], o[e + 1], true);
           if constexpr (NE == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
           else *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
         }
@@ -1317,6 +1333,18 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   //      is in flight and the block ids of round r+2 are being loaded ----
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  // wait for everything but the round just issued (d): its page loads, plus its
+  // query-row loads when it opens a segment; a fixed LPR would make the wave
+  // wait for part of d itself, one full memory latency at every segment start
+  const int nq = p.q_slot >> 10;              // query-row loads of a segment (1 to 4)
+  auto wait_issued = [&](const Desc<CH>& d) {
+    if (!(d.info & kNp)) wait_vmcnt<0>();
+    else if (!(d.info & kFirst)) wait_vmcnt<SG::LPR>();
+    else if (nq <= 1) wait_vmcnt<SG::LPR + 1>();
+    else if (nq == 2) wait_vmcnt<SG::LPR + 2>();
+    else if (nq == 3) wait_vmcnt<SG::LPR + 3>();
+    else wait_vmcnt<SG::LPR + 4>();
+  };
   Desc<CH> da = next();
   if (da.info & kNp) {
     Desc<CH> dn = next();
@@ -1326,16 +1354,14 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       if (dn.info & kNp) issue(dn, S1{});
       db = dn;
       dn = next();
-      if (db.info & kNp) wait_vmcnt<SG::LPR>();
-      else wait_vmcnt<0>();
+      wait_issued(db);
       compute(da, S0{});
       if (!(db.info & kNp)) break;
 
       if (dn.info & kNp) issue(dn, S0{});
       da = dn;
       dn = next();
-      if (da.info & kNp) wait_vmcnt<SG::LPR>();
-      else wait_vmcnt<0>();
+      wait_issued(da);
       compute(db, S1{});
       if (!(da.info & kNp)) break;
     }

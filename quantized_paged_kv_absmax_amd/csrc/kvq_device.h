@@ -125,6 +125,28 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// max / sum of v over the lane pairs (l, l ^ 16), or (l, l ^ 32), through the
+// gfx950 row-swap instructions instead of the LDS crossbar.  Swapping v with
+// itself, v_permlane16_swap leaves rows (r0, r0, r2, r2) in one result and
+// (r1, r1, r3, r3) in the other; v_permlane32_swap leaves (lo, lo) and (hi, hi).
+// Both lanes of a pair combine the two values in the same order.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, 64); }
 
 }  // namespace kvq
