@@ -415,12 +415,8 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
   const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = grp; j < P; j += NG) {
-    // branch-free, so the three loads go out together
-    const float mj = m[(size_t)j * Hq];
-    const float lj = l[(size_t)j * Hq];
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)j * Hq * D + 4 * ln);
-    const bool ok = (mj != -INFINITY);        // -inf: a piece with no valid token
+  auto combine = [&](float mj, float lj, const float4& v) {
+    const bool ok = (mj != -INFINITY);        // -inf: past P, or a piece with no valid token
     const float Mn = ok ? fmaxf(M, mj) : M;
     const float sc = (Mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
     const float f = ok ? __builtin_amdgcn_exp2f(mj - Mn) : 0.0f;
@@ -430,6 +426,31 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
     acc.w = acc.w * sc + (ok ? f * v.w : 0.0f);
     den = den * sc + (ok ? f * lj : 0.0f);
     M = Mn;
+  };
+  if (P <= NG) {
+    // at most one piece per group (branch-free, so the three loads go out together)
+    const size_t jj = (size_t)min(grp, P - 1);
+    const float mj = (grp < P) ? m[jj * Hq] : -INFINITY;
+    const float lj = l[jj * Hq];
+    const float4 v = *reinterpret_cast<const float4*>(o + jj * Hq * D + 4 * ln);
+    combine(mj, lj, v);
+  } else {
+    // eight pieces per group and pass, their loads all in flight before any is
+    // used: a sequence cut into hundreds of pieces is then a few round trips
+    for (int j0 = grp; j0 < P; j0 += 8 * NG) {
+      float mj[8], lj[8];
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * NG;
+        const size_t jj = (size_t)min(j, P - 1);
+        mj[u] = (j < P) ? m[jj * Hq] : -INFINITY;
+        lj[u] = l[jj * Hq];
+        v[u] = *reinterpret_cast<const float4*>(o + jj * Hq * D + 4 * ln);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) combine(mj[u], lj[u], v[u]);
+    }
   }
   __shared__ float4 s_acc[NG][LPG];
   __shared__ float s_m[NG], s_den[NG];
