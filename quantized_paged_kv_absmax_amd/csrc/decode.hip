@@ -703,15 +703,31 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     return L;
   };
 
-  // ---- pages of every sequence: their total T fixes the chunk size ----
+  // ---- pages of every sequence: their total T fixes the chunk size.  Batches
+  //      of up to NR groups of 64 stay in registers (lane j of group r holds
+  //      sequence 64 r + j), their lengths loaded all at once; larger batches
+  //      are scanned group by group and reloaded where needed ----
+  constexpr int NR = 4;
+  const bool in_regs = B <= 64 * NR;
+  int lr[NR], nr[NR], ir[NR];   // length, pages, inclusive page prefix
   int T = 0;
-  int l0 = 0, n0 = 0, i0 = 0;   // B <= 64: length, pages, inclusive page prefix of sequence `lane`
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int L = load_len(b0 + lane, counter);
-    const int np = (L + 15) >> 4;
-    const int inc = wave_incl_sum(np);
-    if (b0 == 0) { l0 = L; n0 = np; i0 = inc; }
-    T += __builtin_amdgcn_readlane(inc, 63);
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) lr[r] = (64 * r < B) ? load_len(64 * r + lane, counter) : 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      nr[r] = (lr[r] + 15) >> 4;
+      ir[r] = T;
+      if (64 * r < B) {
+        ir[r] += wave_incl_sum(nr[r]);
+        T = __builtin_amdgcn_readlane(ir[r], 63);
+      }
+    }
+  } else {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int L = load_len(b0 + lane, counter);
+      T += __builtin_amdgcn_readlane(wave_incl_sum((L + 15) >> 4), 63);
+    }
   }
   int C = p.chunk_pages;
   if (C == 0) C = max(p.min_chunk, (T + p.n_chunks - 1) / p.n_chunks);
@@ -725,10 +741,14 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   //      their position; those at the very end to the last chunk) ----
   auto starts_here = [&](int np, int inc) { return inc > x0 || (np == 0 && inc >= x0); };
   int bs = 0, ex_bs = 0;
-  if (B <= 64) {
-    const uint64_t before = __builtin_amdgcn_ballot_w64(lane < B && !starts_here(n0, i0));
-    bs = popc64(before);
-    ex_bs = __builtin_amdgcn_readlane(i0 - n0, bs & 63);
+  if (in_regs) {
+    // the sequences before the chunk form a prefix of the batch
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (64 * r < B) bs += popc64(__builtin_amdgcn_ballot_w64(64 * r + lane < B && !starts_here(nr[r], ir[r])));
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (r == (bs >> 6)) ex_bs = __builtin_amdgcn_readlane(ir[r] - nr[r], bs & 63);
   } else {
     int carry = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
@@ -753,10 +773,22 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     const int sb = bs + lane;
     const bool wv = sb < B;
     if (from_regs) {
+      // sequence bs + j sits in group (bs >> 6) or the next one, at lane sb & 63
+      const int g0 = bs >> 6;
+      int la = 0, na = 0, xa = 0, lb = 0, nb = 0, xb = 0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (r == g0) { la = lr[r]; na = nr[r]; xa = ir[r] - nr[r]; }
+        if (r == g0 + 1) { lb = lr[r]; nb = nr[r]; xb = ir[r] - nr[r]; }
+      }
       const int src = sb & 63;
-      wL = __shfl(l0, src, 64);
-      wnp = __shfl(n0, src, 64);
-      wex = __shfl(i0 - n0, src, 64);
+      const bool second = (sb >> 6) != g0;
+      const int ta = __shfl(la, src, 64), tb = __shfl(lb, src, 64);
+      const int ua = __shfl(na, src, 64), ub = __shfl(nb, src, 64);
+      const int va = __shfl(xa, src, 64), vb = __shfl(xb, src, 64);
+      wL = second ? tb : ta;
+      wnp = second ? ub : ua;
+      wex = second ? vb : va;
     } else {
       wL = load_len(sb, false);
       wnp = (wL + 15) >> 4;
@@ -788,7 +820,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       }
     }
   };
-  make_window(B <= 64);
+  make_window(in_regs);
 
   // ---- per-wave constants: logit and output scales ----
   float kfac = p.sm_log2;

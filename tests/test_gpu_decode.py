@@ -124,11 +124,12 @@ def test_edge_lengths_and_group_sizes(kd, vd, D, Hq, Hkv):
         assert torch.isfinite(out).all()           # NaN-coded unused slots never leak
 
 
-@pytest.mark.parametrize("kd,vd", [("int8", "int8"), ("int4", "int4")])
-def test_many_short_sequences(kd, vd):
+@pytest.mark.parametrize("kd,vd,nseq", [("int8", "int8", 150), ("int4", "int4", 150), ("int8", "int8", 300)])
+def test_many_short_sequences(kd, vd, nseq):
     # 150 sequences of 0..40 tokens: more sequences than lanes of a wave, and with
-    # 2048-token chunks (128 pages) a chunk spans more than 64 sequences
-    lens = tuple((7 * i) % 41 for i in range(150))
+    # 2048-token chunks (128 pages) a chunk spans more than 64 sequences; 300
+    # sequences: more than the kernel keeps in registers, so it rescans lengths
+    lens = tuple((7 * i) % 41 for i in range(nseq))
     w, inp = _small(Hq=8, Hkv=2, D=128, lens=lens, kd=kd, vd=vd)
     r = build_library_cache(w, inp)
     o = build_oracle_cache(w, inp)
@@ -139,7 +140,7 @@ def test_many_short_sequences(kd, vd):
         out = library_decode(r, inp, partition=part, out_dtype="f32")
         torch.cuda.synchronize()
         mx, nbad = gate_errors(out, ref, "f32")
-        log(f"[short {kd}/{vd}] partition={part} max|err|={mx:.3e}")
+        log(f"[short {kd}/{vd} x{nseq}] partition={part} max|err|={mx:.3e}")
         assert nbad == 0
         assert (out[zero] == 0).all()
 
