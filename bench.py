@@ -392,7 +392,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
-        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "bf16", "int4", "longctx_int8"]
+        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "longctx_int8"]
         if args.only:
             names = [n for n in args.only.split(",") if n]
         for name in names:
@@ -408,6 +408,11 @@ def main():
             del g2
             torch.cuda.empty_cache()
 
+    # capacity: Llama-3-8B's cache (32 layers, 8 KV heads, head_dim 128) in 240 GiB of HBM
+    cap_budget = 240 << 30
+    cap = {d: kvq.kvq_blocks_in_budget(cap_budget, d, d, 8, 128, 32) for d in ("bf16", "int8", "e4m3", "int4")}
+    extras["capacity_llama3_8b_240GiB"] = {"blocks": cap, "tokens": {d: 16 * n for d, n in cap.items()},
+                                           "ratio_vs_bf16": {d: round(n / cap["bf16"], 4) for d, n in cap.items()}}
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     w = WORKLOADS_DESC
     line = {

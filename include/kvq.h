@@ -214,6 +214,28 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       void* workspace, size_t workspace_bytes, int32_t out_dtype,
                                       void* out, int32_t* err_count, void* stream);
 
+/*
+ * kvq_cache_block_bytes — bytes one block of one layer's cache takes: K and V
+ * rows of block_size tokens for num_kv_heads heads, plus the INT4 (scale, zero
+ * point) metadata, exactly what a kvq_cache of that geometry holds per block
+ * (per-tensor / per-KV-head scales are O(num_kv_heads) per layer and not
+ * counted).  Row bytes: 2*head_dim (BF16), head_dim (INT8 / FP8),
+ * head_dim/2 + 8 (INT4 codes and metadata).  Host only, no GPU call; 0 for an
+ * unsupported dtype or a non-positive size.
+ */
+uint64_t kvq_cache_block_bytes(int32_t k_dtype, int32_t v_dtype, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size);
+
+/*
+ * kvq_blocks_in_budget — whole cache blocks (block_size tokens, num_layers
+ * layers, all KV heads) that fit in budget_bytes: the "GPU blocks" count of the
+ * L4 benchmark table in vLLM PR 4893, where an 8-bit KV cache holds exactly
+ * twice the blocks of a 16-bit one.  floor(budget_bytes / (num_layers *
+ * kvq_cache_block_bytes(...))).  Host only; -1 for invalid arguments.
+ */
+int64_t kvq_blocks_in_budget(uint64_t budget_bytes, int32_t k_dtype, int32_t v_dtype, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t num_layers, int32_t block_size);
+
 /* Human-readable name of a status code (static storage). */
 const char* kvq_status_string(int32_t status);
 

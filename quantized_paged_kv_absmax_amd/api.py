@@ -122,6 +122,17 @@ def kvq_convert_cache(cache, k_src, v_src, first_block=0, num_blocks=None, strea
     check(st, "kvq_convert_cache")
 
 
+def kvq_cache_block_bytes(k_dtype, v_dtype, num_kv_heads, head_dim, block_size=16):
+    """Bytes of one block of one layer's cache (K + V rows, INT4 metadata); 0 if unsupported."""
+    return int(_lib.load().kvq_cache_block_bytes(_dt(k_dtype), _dt(v_dtype), num_kv_heads, head_dim, block_size))
+
+
+def kvq_blocks_in_budget(budget_bytes, k_dtype, v_dtype, num_kv_heads, head_dim, num_layers, block_size=16):
+    """Whole blocks of num_layers layers that fit in budget_bytes; -1 for invalid arguments."""
+    return int(_lib.load().kvq_blocks_in_budget(int(budget_bytes), _dt(k_dtype), _dt(v_dtype), num_kv_heads,
+                                                head_dim, num_layers, block_size))
+
+
 def kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition=0):
     return int(_lib.load().kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                                      partition))

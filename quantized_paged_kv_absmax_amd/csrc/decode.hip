@@ -647,6 +647,10 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // BF16 V, and INT4 V, whose weights p_t s_t carry the token's scale and would
   // leave fp16's range (or its precision) for very large or very small scales
   constexpr bool WBF = (VT == DT_BF16 || VT == DT_INT4);
+  // every PV weight goes in as hi + lo (fp16 pairs for INT8 / FP8 V): a single
+  // rounded weight carries 2^-11 relative error, which a peaked softmax over
+  // large V values does not average away
+  constexpr bool WSPLIT = true;
   constexpr bool V_NAN = (VT == DT_E4M3 || VT == DT_E5M2 || VT == DT_BF16);  // codes that can decode to NaN/Inf
   constexpr bool KI8 = (KT == DT_INT8 || KT == DT_INT4);   // integer QK path
   constexpr int NSI = D / 64;                               // its k-steps (16 codes each)
@@ -1217,7 +1221,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < CH; i += 2) {
       u32x4 aop;
-      u32x4 aop_lo;   // bf16 weights: w = w_hi + w_lo (w_hi alone carries only 8 bits)
+      u32x4 aop_lo;   // weights w = w_hi + w_lo (w_hi alone carries 8 or 11 bits)
       u32x2 vop[2][NE];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -1266,9 +1270,9 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         }
         aop[2 * h2] = a0;
         aop[2 * h2 + 1] = a1;
-        if constexpr (VBF) {
-          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
-          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
+        if constexpr (VT != DT_INT4 && (WBF || WSPLIT)) {
+          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, WBF), pr[1] - unpack_hi(a0, WBF), WBF);
+          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, WBF), pr[3] - unpack_hi(a1, WBF), WBF);
         }
 
         v_operands<VT, D>(vw, vop[h2]);
@@ -1288,13 +1292,13 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       for (int e = 0; e < NE; ++e) {
         const u32x4 bop = {vop[0][e][0], vop[0][e][1], vop[1][e][0], vop[1][e][1]};
         oacc[e] = mfma_pv2<WBF>(aop, bop, oacc[e]);
-        if constexpr (WBF) oacc[e] = mfma_pv2<WBF>(aop_lo, bop, oacc[e]);
+        if constexpr (WBF || WSPLIT) oacc[e] = mfma_pv2<WBF>(aop_lo, bop, oacc[e]);
       }
       {
         constexpr uint32_t one2 = WBF ? 0x3F803F80u : 0x3C003C00u;   // bf16 / fp16 1.0 pairs
         const u32x4 ones = {one2, one2, one2, one2};
         sacc = mfma_pv2<WBF>(aop, ones, sacc);
-        if constexpr (WBF) sacc = mfma_pv2<WBF>(aop_lo, ones, sacc);
+        if constexpr (WBF || WSPLIT) sacc = mfma_pv2<WBF>(aop_lo, ones, sacc);
       }
     }
   };

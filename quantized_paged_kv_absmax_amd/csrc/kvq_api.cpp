@@ -239,6 +239,26 @@ const char* kvq_status_string(int32_t status) {
   }
 }
 
+uint64_t kvq_cache_block_bytes(int32_t k_dtype, int32_t v_dtype, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size) {
+  if (!valid_store_dtype(k_dtype) || !valid_store_dtype(v_dtype)) return 0;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || (head_dim & 1)) return 0;
+  auto row = [&](int32_t d) -> uint64_t {
+    if (d == KVQ_BF16) return 2ull * head_dim;
+    if (d == KVQ_INT4_ASYM) return (uint64_t)head_dim / 2 + 8;   // codes + fp32 (scale, zero point)
+    return (uint64_t)head_dim;
+  };
+  return (row(k_dtype) + row(v_dtype)) * (uint64_t)num_kv_heads * (uint64_t)block_size;
+}
+
+int64_t kvq_blocks_in_budget(uint64_t budget_bytes, int32_t k_dtype, int32_t v_dtype, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t num_layers, int32_t block_size) {
+  if (num_layers <= 0) return -1;
+  const uint64_t per = kvq_cache_block_bytes(k_dtype, v_dtype, num_kv_heads, head_dim, block_size);
+  if (per == 0) return -1;
+  return (int64_t)(budget_bytes / (per * (uint64_t)num_layers));
+}
+
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 
 }  // extern "C"

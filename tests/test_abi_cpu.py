@@ -127,3 +127,40 @@ def test_write_convert_calibrate_argument_errors():
     assert lib.kvq_calibrate_scales(FAKE, 10, 2, 100, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
     assert lib.kvq_calibrate_scales(None, 10, 2, 128, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_NULL
     assert lib.kvq_calibrate_scales(FAKE + 4, 10, 2, 128, _lib.PER_TENSOR, _lib.INT8, FAKE, FAKE, None) == _lib.ERR_ALIGN
+
+
+def test_capacity_accounting():
+    # vLLM PR 4893's L4 table: at one memory budget the block count scales with
+    # 1 / (KV bytes per element); the library's count equals the oracle's for every
+    # dtype pair, and a PagedKVCache holds exactly that many bytes per block
+    import json
+
+    import quantized_paged_kv_absmax_amd as kvq
+    from oracle import codecs as oc
+
+    dts = ["bf16", "int8", "e4m3", "e5m2", "int4"]
+    for D in (64, 128):
+        for kd in dts:
+            for vd in dts:
+                if (kd == "int4") != (vd == "int4"):
+                    continue
+                per = kvq.kvq_cache_block_bytes(kd, vd, 8, D)
+                assert per == oc.kv_bytes_per_token_head(kd, vd, D) * 8 * 16, (kd, vd, D)
+                for budget in (0, per - 1, per, 10 * per + 7, 240 << 30):
+                    assert kvq.kvq_blocks_in_budget(budget, kd, vd, 8, D, 32) == \
+                        oc.blocks_in_budget(budget, kd, vd, D, 8, 32), (kd, vd, D, budget)
+                c = kvq.PagedKVCache(3, 8, D, kd, vd, device="cpu")
+                held = c.k_pages.numel() + c.v_pages.numel()
+                held += sum(4 * m.numel() for m in (c.k_meta, c.v_meta) if m is not None)
+                assert held == 3 * per, (kd, vd, D)
+    # Llama-3-8B's cache (32 layers, 8 KV heads, head_dim 128) in 240 GiB of HBM
+    budget = 240 << 30
+    n = {d: kvq.kvq_blocks_in_budget(budget, d, d, 8, 128, 32) for d in ("bf16", "e5m2", "e4m3", "int8", "int4")}
+    assert n["e5m2"] == n["e4m3"] == n["int8"] == 2 * n["bf16"]
+    assert abs(n["int4"] / n["bf16"] - 256 / 72) < 1e-3
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "l4_gpu_blocks.json")))["rows"]
+    assert g[1]["gpu_blocks"] / g[0]["gpu_blocks"] == n["e5m2"] / n["bf16"] == 2.0
+    # invalid arguments
+    assert kvq.kvq_cache_block_bytes(9, 1, 8, 128) == 0
+    assert kvq.kvq_cache_block_bytes("int8", "int8", 0, 128) == 0
+    assert kvq.kvq_blocks_in_budget(budget, "int8", "int8", 8, 128, 0) == -1

@@ -21,6 +21,8 @@ CASES = {
     "fp8_e4m3_s1": dict(B=6),
     "fp8_e5m2": dict(B=6),
     "fp8_hybrid": dict(B=6),
+    "fp8_e4m3_head": dict(B=6),
+    "fp8_e5m2_cal": dict(B=6),
     "longctx_int8": dict(B=2, lens=("uniform", 1000, 3000)),
     "int4": dict(B=8, lens=("uniform", 20, 1500)),
     "bf16": dict(B=6, lens=("uniform", 20, 1500)),

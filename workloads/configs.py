@@ -13,6 +13,10 @@ block_size 16):
   fp8_*          B=256, L=768 (512 prompt + 256 decoded), 32/8/128; K channels as
                  above; e4m3/e4m3 (scale 1.0 or absmax/448), e5m2/e5m2 (1.0),
                  e4m3-K (1.0 or absmax/448) with int8-V (absmax/127).
+  fp8_e4m3_head  as fp8_e4m3, with per-KV-head absmax/448 scales for K and V over
+                 the prompt; every (K or V, head, channel) has its own standard
+                 deviation from LogNormal(0, 0.5), so the heads' scales differ.
+  fp8_e5m2_cal   as fp8_e5m2, with per-tensor absmax/57344 scales over the prompt.
   longctx_int8   B=8, lengths U[32768, 131072], Hq=64, Hkv=8, D=128, INT8
                  per-KV-head scales calibrated on 64 synthetic 2048-token
                  sequences; every (K or V, head, channel) has its own standard
@@ -86,6 +90,11 @@ WORKLOADS = {
     "fp8_hybrid": Workload("fp8_hybrid", 3, 256, 32, 8, 128, ("fixed", (768,)), "e4m3", "int8",
                            k_scale_mode="absmax", v_scale_mode="absmax",
                            k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
+    "fp8_e4m3_head": Workload("fp8_e4m3_head", 6, 256, 32, 8, 128, ("fixed", (768,)), "e4m3", "e4m3",
+                              k_gran="per_kv_head", v_gran="per_kv_head", lognormal_sigma=0.5,
+                              k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
+    "fp8_e5m2_cal": Workload("fp8_e5m2_cal", 7, 256, 32, 8, 128, ("fixed", (768,)), "e5m2", "e5m2",
+                             k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
     "longctx_int8": Workload("longctx_int8", 4, 8, 64, 8, 128, ("uniform", 32768, 131072),
                              k_gran="per_kv_head", v_gran="per_kv_head", lognormal_sigma=0.5,
                              calib="set", calib_set=(64, 2048), new_tokens=1, partition=512),
