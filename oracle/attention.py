@@ -19,6 +19,9 @@ Split form: positions are cut into partitions of ``partition`` tokens; each
 gives (m_j, l_j, acc_j) = (max z, sum exp(z - m_j), sum exp(z - m_j) v_hat), and
       o = sum_j exp(m_j - M) acc_j / sum_j exp(m_j - M) l_j,   M = max_j m_j.
 
+Several query tokens per sequence (``verify``): token i of the last n_q
+positions attends causally to positions 0..L_b - n_q + i.
+
 Pins (tests/test_oracle_attention.py): q = 0 gives the mean of v_hat; one
 token gives v_hat_0; adding a constant to every logit changes nothing; a
 permuted page pool gives bit-identical output to the contiguous order; g = 1
@@ -66,6 +69,45 @@ def decode(cache, q_bits, block_tables, seq_lens, softmax_scale, heads=None, seq
         for h in hs:
             c = col[h // g]
             out[b, h] = _attend(q[b, h], K[:, c, :], V[:, c, :], sm)
+    return out
+
+
+def verify(cache, q_bits, n_q, block_tables, seq_lens, softmax_scale, heads=None, seqs=None):
+    """Several query tokens per sequence over the paged cache, causally
+    -> float64 [B * n_q][Hq][D].
+
+    The multi-token form of the same paged attention (the row of the survey's
+    next steps built on vLLM PR 4893's side note on attention backends, which
+    leaves quantised-KV attention with several query tokens to the paged
+    kernel): speculative verification or a prefill chunk.  The last n_q
+    positions of sequence b are its query tokens; row t = b * n_q + i is token
+    i, at position p = L_b - n_q + i, and attends to positions 0..p of the cache
+    (its own and every earlier one), exactly as ``decode`` with L = p + 1.
+    p < 0 (a sequence shorter than n_q) gives a zero row.  ``heads`` / ``seqs``
+    restrict the work (other rows NaN).
+    """
+    q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
+    T, Hq, D = q.shape
+    B = T // n_q
+    g = Hq // cache.H
+    sm = float(np.float32(softmax_scale))
+    out = np.full((T, Hq, D), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        hs = range(Hq) if heads is None else heads
+        kvs = sorted({h // g for h in hs})
+        col = {kv: i for i, kv in enumerate(kvs)}
+        if L > 0:
+            K = cache.gather(block_tables[b], L, "k", kvs).astype(np.float64)
+            V = cache.gather(block_tables[b], L, "v", kvs).astype(np.float64)
+        for i in range(n_q):
+            t, pos = b * n_q + i, L - n_q + i
+            for h in hs:
+                if pos < 0:
+                    out[t, h] = 0.0
+                    continue
+                c = col[h // g]
+                out[t, h] = _attend(q[t, h], K[:pos + 1, c, :], V[:pos + 1, c, :], sm)
     return out
 
 

@@ -116,3 +116,74 @@ def test_gqa_equals_repeated_kv_heads():
     rep.write(np.repeat(inp.k_bits, g, axis=1), np.repeat(inp.v_bits, g, axis=1), inp.slot_mapping)
     out2 = oa.decode(rep, inp.q_bits, inp.block_tables, inp.seq_lens, 0.125)
     assert np.array_equal(out, out2)
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per sequence (causal)
+# ---------------------------------------------------------------------------
+
+
+def _verify_q(inp, n_q, seed=21):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((inp.w.B * n_q, inp.w.Hq, inp.w.D)).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kd,vd", [("int8", "int8"), ("e4m3", "e5m2"), ("int4", "int4")])
+def test_verify_matches_torch_sdpa_causal_fp64(kd, vd):
+    # torch's scaled_dot_product_attention with an explicit mask: query token i of
+    # sequence b (position L - n_q + i) sees cache positions 0..L - n_q + i
+    inp = _inputs(B=3, lens=("fixed", (5, 40, 77)))
+    c = _cache(inp, kd, vd)
+    n_q = 5
+    qb = _verify_q(inp, n_q)
+    sm = float(np.float32(1 / np.sqrt(64)))
+    out = oa.verify(c, qb, n_q, inp.block_tables, inp.seq_lens, sm)
+    g = inp.w.Hq // inp.w.Hkv
+    q = torch.from_numpy(codecs.bf16_to_f32(qb).astype(np.float64))
+    for b in range(inp.w.B):
+        L = int(inp.seq_lens[b])
+        K = torch.from_numpy(c.gather(inp.block_tables[b], L, "k").astype(np.float64))
+        V = torch.from_numpy(c.gather(inp.block_tables[b], L, "v").astype(np.float64))
+        K = K.permute(1, 0, 2).repeat_interleave(g, dim=0)                   # [Hq][L][D]
+        V = V.permute(1, 0, 2).repeat_interleave(g, dim=0)
+        pos = torch.arange(L - n_q, L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos                                # [n_q][L]
+        qq = q[b * n_q:(b + 1) * n_q].permute(1, 0, 2)                         # [Hq][n_q][D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, K, V, attn_mask=mask, scale=sm)
+        np.testing.assert_allclose(out[b * n_q:(b + 1) * n_q], ref.permute(1, 0, 2).numpy(), rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_verify_rows_are_truncated_decodes():
+    # row i of sequence b is the single-query decode of query i over the first
+    # L - n_q + i + 1 positions; one query token per sequence is the decode itself
+    inp = _inputs(B=3, lens=("fixed", (3, 40, 77)))
+    c = _cache(inp, "e4m3", "int8")
+    n_q = 4
+    qb = _verify_q(inp, n_q)
+    out = oa.verify(c, qb, n_q, inp.block_tables, inp.seq_lens, 0.125)
+    for i in range(n_q):
+        lens = inp.seq_lens - n_q + i + 1
+        ref = oa.decode(c, qb[i::n_q], inp.block_tables, lens, 0.125)
+        assert np.array_equal(out[i::n_q], ref), i
+    one = oa.verify(c, inp.q_bits, 1, inp.block_tables, inp.seq_lens, 0.125)
+    assert np.array_equal(one, oa.decode(c, inp.q_bits, inp.block_tables, inp.seq_lens, 0.125))
+    # sequence 0 has 3 tokens: its first query token (position -1) sees nothing
+    assert (out[0] == 0).all() and np.isfinite(out[1]).all()
+
+
+def test_verify_zero_query_gives_prefix_mean():
+    inp = _inputs(B=2, lens=("fixed", (20, 33)))
+    c = _cache(inp)
+    n_q = 3
+    q0 = np.zeros((inp.w.B * n_q, inp.w.Hq, inp.w.D), np.uint16)
+    out = oa.verify(c, q0, n_q, inp.block_tables, inp.seq_lens, 0.125)
+    g = inp.w.Hq // inp.w.Hkv
+    for b in range(2):
+        L = int(inp.seq_lens[b])
+        V = c.gather(inp.block_tables[b], L, "v").astype(np.float64)
+        for i in range(n_q):
+            for h in range(inp.w.Hq):
+                np.testing.assert_allclose(out[b * n_q + i, h], V[:L - n_q + i + 1, h // g].mean(axis=0),
+                                           rtol=0, atol=1e-14)
