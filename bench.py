@@ -145,7 +145,7 @@ def kv_bytes(inp):
 
 def decode_source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "kvq_device.h"):
+    for f in ("decode_kernel.h", "decode.hip", "kvq_device.h"):
         h.update(open(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -238,9 +238,9 @@ class GpuWorkload:
             if km is not None:
                 s.k_meta, s.v_meta = km.data_ptr(), vm.data_ptr()
             self.structs.append(s)
-        ws = kvq.kvq_decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, inp.max_seq_len, w.partition)
+        ws = kvq.kvq_verify_workspace_size(w.B, w.n_q, w.Hq, w.Hkv, w.D, inp.max_seq_len, w.partition)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
-        self.out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=device)
+        self.out = torch.empty((w.B * w.n_q, w.Hq, w.D), dtype=torch.bfloat16, device=device)
         self.kv_bytes = kv_bytes(inp)
         torch.cuda.synchronize()
 
@@ -250,6 +250,11 @@ class GpuWorkload:
             self.kvq.kvq_cache_write(self.cache, self.k_new, self.v_new, self.slot_new, struct=self.structs[i % self.R])
 
     def decode(self, i):
+        if self.w.n_q > 1:
+            self.kvq.kvq_paged_attention_verify(self.cache, self.q, self.w.n_q, self.bt, self.sl, self.inp.max_seq_len,
+                                                self.sm, partition=self.w.partition, workspace=self.ws, out=self.out,
+                                                struct=self.structs[i % self.R])
+            return
         self.kvq.kvq_paged_attention_decode(self.cache, self.q, self.bt, self.sl, self.inp.max_seq_len, self.sm,
                                             partition=self.w.partition, workspace=self.ws, out=self.out,
                                             struct=self.structs[i % self.R])
@@ -392,7 +397,8 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
-        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "longctx_int8"]
+        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "longctx_int8",
+                 "verify16_int8"]
         if args.only:
             names = [n for n in args.only.split(",") if n]
         for name in names:

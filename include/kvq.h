@@ -215,6 +215,41 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       void* out, int32_t* err_count, void* stream);
 
 /*
+ * kvq_paged_attention_verify — several query tokens per sequence over the
+ * cache, causally: speculative-decoding verification or a prefill chunk whose
+ * K/V rows are already written.
+ *
+ * The multi-token form of the paged attention above (vLLM PR 4893's side note
+ * on attention backends leaves quantised-KV attention with more than one query
+ * to the paged kernel).  The last n_q positions of sequence b are its query
+ * tokens: token i (row b * n_q + i of q and out) sits at position
+ * p = seq_lens[b] - n_q + i and attends to cache positions 0..p; p < 0 gives a
+ * zero row.  Per KV head, the n_q * g (query token, head) rows run as tiles of
+ * 16 MFMA columns, one wave per (chunk, KV head, tile); the work split, the
+ * workspace and the reduce are those of kvq_paged_attention_decode, which is
+ * this call with n_q = 1.
+ *   q      (device) bf16 [batch * n_q][num_q_heads][head_dim], token-major
+ *   n_q    >= 1, n_q * num_q_heads <= 65535
+ *   out    (device) [batch * n_q][num_q_heads][head_dim] of out_dtype
+ *   workspace  >= kvq_verify_workspace_size(...) bytes (same rules as decode)
+ * Other arguments, errors and dtype pairs as kvq_paged_attention_decode.
+ */
+kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q, int32_t n_q,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                      void* workspace, size_t workspace_bytes, int32_t out_dtype,
+                                      void* out, int32_t* err_count, void* stream);
+
+/*
+ * kvq_verify_workspace_size — device workspace bytes kvq_paged_attention_verify
+ * needs (0 when it runs as a single chunk, or for invalid arguments).  The
+ * decode layout with n_q * num_q_heads rows per slot in place of num_q_heads.
+ */
+size_t kvq_verify_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t partition);
+
+/*
  * kvq_cache_block_bytes — bytes one block of one layer's cache takes: K and V
  * rows of block_size tokens for num_kv_heads heads, plus the INT4 (scale, zero
  * point) metadata, exactly what a kvq_cache of that geometry holds per block

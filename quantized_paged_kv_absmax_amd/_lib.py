@@ -21,8 +21,8 @@ DTYPES = {"bf16": BF16, "auto": BF16, "int8": INT8, "e4m3": FP8_E4M3, "fp8": FP8
 GRANULARITIES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD, "per_token_head": PER_TOKEN_HEAD}
 
 EXPORTS = ("kvq_calibrate_scales", "kvq_cache_write", "kvq_convert_cache", "kvq_decode_workspace_size",
-           "kvq_paged_attention_decode", "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string",
-           "kvq_abi_version")
+           "kvq_paged_attention_decode", "kvq_paged_attention_verify", "kvq_verify_workspace_size",
+           "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string", "kvq_abi_version")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -60,6 +60,10 @@ def load():
     lib.kvq_decode_workspace_size.restype = SZ
     lib.kvq_paged_attention_decode.argtypes = [CP, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
     lib.kvq_paged_attention_decode.restype = I32
+    lib.kvq_paged_attention_verify.argtypes = [CP, P, I32, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
+    lib.kvq_paged_attention_verify.restype = I32
+    lib.kvq_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.kvq_verify_workspace_size.restype = SZ
     lib.kvq_cache_block_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.kvq_cache_block_bytes.restype = ctypes.c_uint64
     lib.kvq_blocks_in_budget.argtypes = [ctypes.c_uint64, I32, I32, I32, I32, I32, I32]

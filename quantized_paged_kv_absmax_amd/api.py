@@ -122,6 +122,43 @@ def kvq_convert_cache(cache, k_src, v_src, first_block=0, num_blocks=None, strea
     check(st, "kvq_convert_cache")
 
 
+def kvq_verify_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition=0):
+    return int(_lib.load().kvq_verify_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                     partition))
+
+
+def kvq_paged_attention_verify(cache, q, n_q, block_tables, seq_lens, max_seq_len, softmax_scale, partition=0,
+                               workspace=None, out_dtype="bf16", out=None, err_count=None, stream=None,
+                               struct=None):
+    """n_q query tokens per sequence, causally: q bf16 [B * n_q][Hq][D] -> out [B * n_q][Hq][D].
+
+    Row b * n_q + i is sequence b's token at position seq_lens[b] - n_q + i; it
+    attends to cache positions up to its own.  Arguments otherwise as
+    kvq_paged_attention_decode.
+    """
+    _need(q, torch.bfloat16, "q")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    T, Hq, D = q.shape
+    B = seq_lens.shape[0]
+    if T != B * n_q:
+        raise ValueError(f"q has {T} rows, expected batch * n_q = {B * n_q}")
+    odt = _dt(out_dtype)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32 if odt == _lib.F32 else torch.bfloat16, device=q.device)
+    need = kvq_verify_workspace_size(B, n_q, Hq, cache.num_kv_heads, D, max_seq_len, partition)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = cache.struct() if struct is None else struct
+    st = _lib.load().kvq_paged_attention_verify(
+        ctypes.byref(s), _ptr(q), int(n_q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
+        int(max_seq_len), Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out),
+        _ptr(err_count), _stream(stream))
+    check(st, "kvq_paged_attention_verify")
+    return out
+
+
 def kvq_cache_block_bytes(k_dtype, v_dtype, num_kv_heads, head_dim, block_size=16):
     """Bytes of one block of one layer's cache (K + V rows, INT4 metadata); 0 if unsupported."""
     return int(_lib.load().kvq_cache_block_bytes(_dt(k_dtype), _dt(v_dtype), num_kv_heads, head_dim, block_size))

@@ -31,7 +31,7 @@ CFLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["kvq_api.cpp", "calibrate.hip", "cache_write.hip", "decode.hip"]
+SOURCES = ["kvq_api.cpp", "calibrate.hip", "cache_write.hip", "decode.hip", "verify.hip"]
 
 
 def _compile(src):

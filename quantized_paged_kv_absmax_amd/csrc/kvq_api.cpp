@@ -76,7 +76,9 @@ struct Split {
   int chunk_pages;   // 0: automatic
 };
 
-Split decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_seq_len, int32_t partition) {
+// n_tiles: waves per (chunk, KV head), one per 16 (query token, head) rows
+Split decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_seq_len, int32_t partition,
+                   int64_t n_tiles = 1) {
   const int64_t bound = batch * ((max_seq_len + 15) / 16);   // pages, at most
   Split sp;
   if (partition > 0) {
@@ -84,7 +86,7 @@ Split decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_seq_len, int
     sp.n_chunks = (bound + sp.chunk_pages - 1) / sp.chunk_pages;
   } else {
     sp.chunk_pages = 0;
-    const int64_t target = (kTargetWaves + num_kv_heads - 1) / num_kv_heads;
+    const int64_t target = (kTargetWaves + num_kv_heads * n_tiles - 1) / (num_kv_heads * n_tiles);
     const int64_t most = (bound + kMinChunk - 1) / kMinChunk;
     sp.n_chunks = target < most ? target : most;
   }
@@ -92,8 +94,8 @@ Split decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_seq_len, int
   return sp;
 }
 
-// Decode workspace, with S = n_chunks + batch piece slots:
-// [m f32 [S][Hq]] [l f32 [S][Hq]] [rec int32 [batch][2]] [acc f32 [S][Hq][D]],
+// Decode workspace, with S = n_chunks + batch piece slots and R = n_q * Hq rows
+// per slot: [m f32 [S][R]] [l f32 [S][R]] [rec int32 [batch][2]] [acc f32 [S][R][D]],
 // each region starting on a 16-byte boundary; none when there is one chunk.
 struct WsLayout {
   int64_t m, l, rec, o, total;
@@ -166,13 +168,20 @@ kvq_status kvq_convert_cache(const kvq_cache* dst, const uint16_t* k_src, const 
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t kvq_verify_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t partition) {
+  if (batch <= 0 || n_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+  if (partition < 0 || partition % 16 != 0) return 0;
+  if (num_q_heads % num_kv_heads != 0 || (int64_t)n_q * num_q_heads > 65535) return 0;
+  const int64_t n_tiles = ((int64_t)n_q * (num_q_heads / num_kv_heads) + 15) / 16;
+  const Split sp = decode_split(batch, num_kv_heads, max_seq_len, partition, n_tiles);
+  if (sp.n_chunks <= 1) return 0;
+  return workspace_layout(batch, (int64_t)n_q * num_q_heads, head_dim, sp.n_chunks).total;
+}
+
 size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition) {
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
-  if (partition < 0 || partition % 16 != 0) return 0;
-  const Split sp = decode_split(batch, num_kv_heads, max_seq_len, partition);
-  if (sp.n_chunks <= 1) return 0;
-  return workspace_layout(batch, num_q_heads, head_dim, sp.n_chunks).total;
+  return kvq_verify_workspace_size(batch, 1, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition);
 }
 
 kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q, const int32_t* block_tables,
@@ -180,6 +189,17 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       int32_t max_seq_len, int32_t num_q_heads, float softmax_scale,
                                       int32_t partition, void* workspace, size_t workspace_bytes,
                                       int32_t out_dtype, void* out, int32_t* err_count, void* stream) {
+  return kvq_paged_attention_verify(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                                    num_q_heads, softmax_scale, partition, workspace, workspace_bytes, out_dtype,
+                                    out, err_count, stream);
+}
+
+kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q, int32_t n_q,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      int32_t num_q_heads, float softmax_scale, int32_t partition, void* workspace,
+                                      size_t workspace_bytes, int32_t out_dtype, void* out, int32_t* err_count,
+                                      void* stream) {
   const kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (!kvq::decode_supported(cache->k_dtype, cache->v_dtype, cache->head_dim)) return KVQ_ERR_UNSUPPORTED;
@@ -188,12 +208,17 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
   if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0) return KVQ_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
   if (partition < 0 || partition % 16 != 0) return KVQ_ERR_SHAPE;
+  if (n_q < 1 || (int64_t)n_q * num_q_heads > 65535) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
   if (!q || !block_tables || !seq_lens || !out) return KVQ_ERR_NULL;
   if (!aligned16(q)) return KVQ_ERR_ALIGN;
   if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_ERR_SHAPE;
   if ((int64_t)batch * (((int64_t)max_seq_len + 15) / 16) > INT32_MAX / 2) return KVQ_ERR_SHAPE;
-  const Split sp = decode_split(batch, cache->num_kv_heads, max_seq_len, partition);
+  const int64_t n_tiles = ((int64_t)n_q * (num_q_heads / cache->num_kv_heads) + 15) / 16;
+  const Split sp = decode_split(batch, cache->num_kv_heads, max_seq_len, partition, n_tiles);
+  if (sp.n_chunks * n_tiles > INT32_MAX / 2) return KVQ_ERR_SHAPE;
+  // the query block of one sequence (n_q * Hq rows) is addressed with 32-bit offsets
+  if ((int64_t)n_q * num_q_heads * cache->head_dim * 2 > INT32_MAX / 2) return KVQ_ERR_SHAPE;
   kvq::DecodeArgs a;
   a.q = q;
   a.block_tables = block_tables;
@@ -202,6 +227,7 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
   a.batch = batch;
   a.max_seq_len = max_seq_len;
   a.num_q_heads = num_q_heads;
+  a.n_q = n_q;
   a.softmax_scale = softmax_scale;
   a.chunk_pages = sp.chunk_pages;
   a.n_chunks = (int)sp.n_chunks;
@@ -209,11 +235,10 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
   a.ws_m = a.ws_l = a.ws_o = nullptr;
   a.ws_rec = nullptr;
   if (sp.n_chunks > 1) {
-    const size_t need = workspace_layout(batch, num_q_heads, cache->head_dim, sp.n_chunks).total;
+    const WsLayout lay = workspace_layout(batch, (int64_t)n_q * num_q_heads, cache->head_dim, sp.n_chunks);
     if (!workspace) return KVQ_ERR_WORKSPACE;
-    if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (workspace_bytes < (size_t)lay.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
-    const WsLayout lay = workspace_layout(batch, num_q_heads, cache->head_dim, sp.n_chunks);
     char* base = static_cast<char*>(workspace);
     a.ws_m = reinterpret_cast<float*>(base + lay.m);
     a.ws_l = reinterpret_cast<float*>(base + lay.l);

@@ -34,13 +34,14 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   const int32_t* seq_lens;
   int batch, max_seq_len, num_q_heads;
+  int n_q;           // query tokens per sequence (1: decode)
   float softmax_scale;
   int chunk_pages;   // pages per chunk, 0: chosen on the device from the total
   int n_chunks;      // chunks in the launch
   int min_chunk;     // smallest automatic chunk
-  float* ws_m;       // [slots][Hq]      (all four NULL when n_chunks == 1)
-  float* ws_l;       // [slots][Hq]
-  float* ws_o;       // [slots][Hq][D]
+  float* ws_m;       // [slots][n_q Hq]      (all four NULL when n_chunks == 1)
+  float* ws_l;       // [slots][n_q Hq]
+  float* ws_o;       // [slots][n_q Hq][D]
   int32_t* ws_rec;   // [B][2]
   int out_f32;
   void* out;

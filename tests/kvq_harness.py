@@ -84,7 +84,11 @@ def build_library_cache(w, inp, device="cuda", calib=None):
 
 
 def library_decode(r, inp, partition=0, out_dtype="f32", err=None):
+    """The workload's attention call: decode, or verify with its n_q query tokens."""
     w = inp.w
+    if w.n_q > 1:
+        return kvq.kvq_paged_attention_verify(r.cache, r.q, w.n_q, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                              partition=partition, out_dtype=out_dtype, err_count=err)
     return kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
                                           partition=partition, out_dtype=out_dtype, err_count=err)
 
@@ -230,8 +234,17 @@ def gate_errors(out, ref, out_dtype):
 
 
 def oracle_decode(oracle_cache, inp, heads=None, seqs=None):
+    if inp.w.n_q > 1:
+        return oa.verify(oracle_cache, inp.q_bits, inp.w.n_q, inp.block_tables, inp.seq_lens,
+                         softmax_scale(inp.w.D), heads=heads, seqs=seqs)
     return oa.decode(oracle_cache, inp.q_bits, inp.block_tables, inp.seq_lens, softmax_scale(inp.w.D),
                      heads=heads, seqs=seqs)
+
+
+def query_rows(inp, seqs):
+    """Rows of q / out that belong to the given sequences (n_q per sequence)."""
+    n = inp.w.n_q
+    return [b * n + i for b in seqs for i in range(n)]
 
 
 def sample_rows(inp, n_seqs, heads_per_seq, seed=0):
@@ -250,5 +263,6 @@ def ceil_div(a, b):
 
 
 __all__ = ["dev_bf16", "build_library_cache", "library_decode", "build_oracle_cache", "build_oracle_cache_sampled",
+           "query_rows",
            "seq_token_rows", "assert_codes_equal",
            "gate_errors", "oracle_decode", "sample_rows", "log", "softmax_scale", "math", "ceil_div"]

@@ -86,6 +86,21 @@ def test_decode_argument_errors():
     assert _decode(_cache(), B=0) == _lib.OK
 
 
+def test_verify_argument_errors():
+    lib = _lib.load()
+
+    def verify(n_q, Hq=4, B=2):
+        c = _cache()
+        return lib.kvq_paged_attention_verify(ctypes.byref(c), FAKE, n_q, FAKE, 8, FAKE, B, 100, Hq, 0.088, 0, None,
+                                              0, _lib.BF16, FAKE, None, None)
+
+    assert verify(0) == _lib.ERR_SHAPE
+    assert verify(-3) == _lib.ERR_SHAPE
+    assert verify(20000, Hq=4) == _lib.ERR_SHAPE          # n_q * Hq above 65535
+    assert verify(4, Hq=5) == _lib.ERR_SHAPE
+    assert verify(4, B=0) == _lib.OK
+
+
 def test_workspace_size():
     lib = _lib.load()
     r16 = lambda x: (x + 15) // 16 * 16
@@ -98,7 +113,7 @@ def test_workspace_size():
     assert lib.kvq_decode_workspace_size(1, 32, 8, 128, 64, 0) == 0               # 4 pages: one chunk
     assert lib.kvq_decode_workspace_size(1, 32, 8, 128, 80, 0) == layout(1, 32, 128, 2)
     assert lib.kvq_decode_workspace_size(64, 32, 8, 128, 4096, 0) == layout(64, 32, 128, 256)
-    assert lib.kvq_decode_workspace_size(64, 32, 3, 128, 4096, 0) == layout(64, 32, 128, 683)
+    assert lib.kvq_decode_workspace_size(64, 33, 3, 128, 4096, 0) == layout(64, 33, 128, 683)
     # explicit partition: ceil(B * ceil(max_seq_len / 16) / (partition / 16)) chunks
     assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 512, 512) == layout(4, 32, 128, 4)
     assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 1100, 256) == layout(4, 32, 128, 18)
@@ -107,6 +122,13 @@ def test_workspace_size():
     assert lib.kvq_decode_workspace_size(4, 32, 8, 128, 512, 24) == 0
     assert lib.kvq_decode_workspace_size(4, 32, 0, 128, 512, 0) == 0
     assert lib.kvq_decode_workspace_size(0, 32, 8, 128, 512, 0) == 0
+    assert lib.kvq_decode_workspace_size(64, 32, 3, 128, 4096, 0) == 0      # Hq not a multiple of Hkv
+    # several query tokens: n_q * Hq rows per slot, chunks for about 2048 waves of
+    # n_tiles = ceil(n_q * g / 16) tiles each
+    assert lib.kvq_verify_workspace_size(64, 1, 32, 8, 128, 4096, 0) == layout(64, 32, 128, 256)
+    assert lib.kvq_verify_workspace_size(64, 16, 32, 8, 128, 4096, 0) == layout(64, 16 * 32, 128, 64)
+    assert lib.kvq_verify_workspace_size(4, 3, 32, 8, 128, 1100, 256) == layout(4, 3 * 32, 128, 18)
+    assert lib.kvq_verify_workspace_size(4, 0, 32, 8, 128, 1100, 256) == 0
 
 
 def test_write_convert_calibrate_argument_errors():

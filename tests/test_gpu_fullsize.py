@@ -20,13 +20,13 @@ import torch
 
 import quantized_paged_kv_absmax_amd as kvq
 from tests.kvq_harness import (assert_codes_equal, build_library_cache, build_oracle_cache_sampled, gate_errors,
-                               library_decode, log, oracle_decode, softmax_scale)
+                               library_decode, log, oracle_decode, query_rows, softmax_scale)
 from workloads import WORKLOADS, make_calibration_set, make_decode_inputs
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ["llama8b_int8", "fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4",
-         "longctx_int8"]
+         "longctx_int8", "verify16_int8"]
 N_SEQS = {"longctx_int8": 2}   # 32K-131K-token sequences: two suffice, four heads each
 N_HEADS = 4
 
@@ -71,24 +71,27 @@ def test_full_size_codes_and_sampled_decode(name):
     log(f"[{name}] codes bit-exact on {len(seqs)} sequences")
 
     of = out.float()
-    nonempty = torch.from_numpy(inp.seq_lens > 0).to(of.device)
+    nonempty = torch.from_numpy(np.repeat(inp.seq_lens > 0, w.n_q)).to(of.device)
     assert bool(torch.isfinite(of[nonempty]).all()), "non-finite output row"
 
     ref = oracle_decode(o, inp, heads=heads, seqs=seqs)
-    got = out[seqs][:, heads]
-    e, bad = gate_errors(got, ref[seqs][:, heads], "bf16")
+    qr = query_rows(inp, seqs)
+    got = out[qr][:, heads]
+    e, bad = gate_errors(got, ref[qr][:, heads], "bf16")
     log(f"[{name}] sampled decode max|err| {e:.2e}, violations {bad}")
     assert bad == 0
 
     # a convex combination of V rows: each output lies within its sequence's V range
     g = w.Hq // w.Hkv
-    for i, b in enumerate(seqs):
+    for i, row in enumerate(qr):
+        b, t = divmod(row, w.n_q)
+        visible = int(inp.seq_lens[b]) - w.n_q + t + 1        # positions the query token sees
         for j, h in enumerate(heads):
-            V = o.gather(inp.block_tables[b], int(inp.seq_lens[b]), "v", [h // g])[:, 0, :].astype(np.float64)
+            V = o.gather(inp.block_tables[b], visible, "v", [h // g])[:, 0, :].astype(np.float64)
             lo, hi = V.min(axis=0), V.max(axis=0)
             x = got[i, j].float().cpu().numpy().astype(np.float64)
             slack = 4e-3 + np.abs(np.stack([lo, hi])).max(axis=0) * 2.0 ** -8
-            assert np.all(x >= lo - slack) and np.all(x <= hi + slack), (b, h)
+            assert np.all(x >= lo - slack) and np.all(x <= hi + slack), (b, t, h)
     del r, out
     torch.cuda.empty_cache()
 

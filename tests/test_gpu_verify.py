@@ -1,0 +1,98 @@
+"""GPU parity of kvq_paged_attention_verify (several query tokens per sequence,
+causal over the paged cache) against the oracle, through the C ABI: format
+pairs, group sizes 1 to 16, tiles of 16 (token, head) columns that split a
+token's heads, sequences shorter than the query block, and forced splits."""
+
+import pytest
+import torch
+
+import quantized_paged_kv_absmax_amd as kvq
+from tests.kvq_harness import (build_library_cache, build_oracle_cache, gate_errors, library_decode, log,
+                               oracle_decode, softmax_scale)
+from workloads import WORKLOADS, make_decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(kd, vd, Hq, Hkv, D, n_q, lens, seed=31):
+    w = WORKLOADS["tiny_int8"].with_(B=len(lens), lens=("fixed", lens), Hq=Hq, Hkv=Hkv, D=D, k_dtype=kd,
+                                     v_dtype=vd, seed=seed, n_q=n_q, new_tokens=0, calib="all")
+    if kd == "int4":
+        w = w.with_(k_gran="per_token_head", v_gran="per_token_head", k_scale_mode="row", v_scale_mode="row",
+                    calib="none")
+    elif kd == "bf16":
+        w = w.with_(k_scale_mode="one", v_scale_mode="one", calib="none")
+    return w, make_decode_inputs(w)
+
+
+# (K, V, Hq, Hkv, D, n_q): g = 4 with 16 tokens (4 tiles), g = 3 (a token's heads
+# cut by a tile edge), g = 8 with odd n_q, g = 16 (one token per tile), g = 1
+CASES = [
+    ("int8", "int8", 8, 2, 128, 16),
+    ("e4m3", "e5m2", 6, 2, 128, 7),
+    ("int4", "int4", 16, 2, 128, 5),
+    ("bf16", "bf16", 16, 1, 64, 3),
+    ("e4m3", "int8", 2, 2, 64, 20),
+]
+
+
+@pytest.mark.parametrize("kd,vd,Hq,Hkv,D,n_q", CASES)
+def test_verify_within_tolerance(kd, vd, Hq, Hkv, D, n_q):
+    lens = (3, n_q, 17, 300, 1000, 1)            # shorter than the query block, equal to it, longer
+    w, inp = _small(kd, vd, Hq, Hkv, D, n_q, lens)
+    r = build_library_cache(w, inp)
+    o = build_oracle_cache(w, inp)
+    ref = oracle_decode(o, inp)
+    for part in (0, 16, 64):
+        for odt in ("f32", "bf16"):
+            out = library_decode(r, inp, partition=part, out_dtype=odt)
+            torch.cuda.synchronize()
+            mx, bad = gate_errors(out, ref, odt)
+            log(f"[verify {kd}/{vd} g={Hq // Hkv} n_q={n_q} D={D}] partition={part} out={odt} max|err|={mx:.3e}")
+            assert bad == 0
+    # rows whose position is below 0 (sequence 0 has 3 tokens) are zero
+    out = library_decode(r, inp, partition=0, out_dtype="f32")
+    assert (out[:n_q - 3] == 0).all()
+
+
+def test_one_query_token_is_decode():
+    w, inp = _small("int8", "int8", 8, 2, 128, 1, (5, 40, 700))
+    r = build_library_cache(w, inp)
+    sm = softmax_scale(w.D)
+    for part in (0, 16):
+        a = kvq.kvq_paged_attention_verify(r.cache, r.q, 1, r.bt, r.sl, inp.max_seq_len, sm, partition=part,
+                                           out_dtype="f32")
+        b = kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, inp.max_seq_len, sm, partition=part,
+                                           out_dtype="f32")
+        assert torch.equal(a, b)
+
+
+def test_each_query_token_is_a_truncated_decode():
+    # token i of a sequence equals a one-token decode of the same query over the
+    # first L - n_q + i + 1 positions (the library against itself, both splits)
+    n_q = 6
+    w, inp = _small("e4m3", "e4m3", 8, 2, 128, n_q, (20, 333, 64))
+    r = build_library_cache(w, inp)
+    sm = softmax_scale(w.D)
+    out = kvq.kvq_paged_attention_verify(r.cache, r.q, n_q, r.bt, r.sl, inp.max_seq_len, sm, out_dtype="f32")
+    for i in range(n_q):
+        lens = (r.sl - n_q + i + 1).to(torch.int32).contiguous()
+        q_i = r.q[i::n_q].contiguous()
+        d = kvq.kvq_paged_attention_decode(r.cache, q_i, r.bt, lens, inp.max_seq_len, sm, out_dtype="f32")
+        torch.cuda.synchronize()
+        diff = (out[i::n_q] - d).abs().max().item()
+        assert diff <= 2e-5, (i, diff)
+
+
+def test_verify16_workload_reduced():
+    w = WORKLOADS["verify16_int8"]
+    inp = make_decode_inputs(w, B=6, lens=("uniform", 16, 1500))
+    r = build_library_cache(w, inp)
+    o = build_oracle_cache(w, inp)
+    ref = oracle_decode(o, inp)
+    for part in (0, 512):
+        out = library_decode(r, inp, partition=part, out_dtype="bf16")
+        torch.cuda.synchronize()
+        mx, bad = gate_errors(out, ref, "bf16")
+        log(f"[verify16_int8 B=6] partition={part} max|err|={mx:.3e}")
+        assert bad == 0

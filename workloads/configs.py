@@ -17,6 +17,9 @@ block_size 16):
                  the prompt; every (K or V, head, channel) has its own standard
                  deviation from LogNormal(0, 0.5), so the heads' scales differ.
   fp8_e5m2_cal   as fp8_e5m2, with per-tensor absmax/57344 scales over the prompt.
+  verify16_int8  the llama8b_int8 cache with 16 query tokens per sequence (the
+                 last 16 positions, written by the step), attending causally:
+                 a prefill chunk or a speculative verification of 15 drafts.
   longctx_int8   B=8, lengths U[32768, 131072], Hq=64, Hkv=8, D=128, INT8
                  per-KV-head scales calibrated on 64 synthetic 2048-token
                  sequences; every (K or V, head, channel) has its own standard
@@ -62,6 +65,7 @@ class Workload:
     calib: str = "prompt"         # prompt | all | set | none
     calib_set: tuple = (0, 0)     # (sequences, tokens each) for calib == "set"
     new_tokens: int = 1           # tokens written by the decode step itself
+    n_q: int = 1                  # query tokens per sequence (>1: the last n_q positions, causally)
     partition: int = 0            # decode work split: 0 = the library's automatic chunks
     from_bf16_cache: bool = False  # cache starts as bf16 pages, then converted
     block_size: int = BLOCK
@@ -95,6 +99,8 @@ WORKLOADS = {
                               k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
     "fp8_e5m2_cal": Workload("fp8_e5m2_cal", 7, 256, 32, 8, 128, ("fixed", (768,)), "e5m2", "e5m2",
                              k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=256),
+    "verify16_int8": Workload("verify16_int8", 8, 64, 32, 8, 128, ("uniform", 512, 4096),
+                              k_outliers=_outliers(8, 128, 0.01), calib="prompt", new_tokens=16, n_q=16),
     "longctx_int8": Workload("longctx_int8", 4, 8, 64, 8, 128, ("uniform", 32768, 131072),
                              k_gran="per_kv_head", v_gran="per_kv_head", lognormal_sigma=0.5,
                              calib="set", calib_set=(64, 2048), new_tokens=1, partition=512),
@@ -133,7 +139,7 @@ def bf16_bits_to_f32(b):
 class DecodeInputs:
     w: Workload
     seq_lens: np.ndarray        # int32 [B]
-    q_bits: np.ndarray          # uint16 [B][Hq][D]
+    q_bits: np.ndarray          # uint16 [B * n_q][Hq][D] (token-major within a sequence)
     k_bits: np.ndarray          # uint16 [Ntok][Hkv][D], token-major, sequences concatenated
     v_bits: np.ndarray          # uint16 [Ntok][Hkv][D]
     cu: np.ndarray              # int64 [B+1] token offsets of each sequence
@@ -242,7 +248,7 @@ def make_decode_inputs(w, B=None, lens=None):
     L64 = seq_lens.astype(np.int64)
     cu = np.concatenate([[0], np.cumsum(L64)]).astype(np.int64)
     ntok = int(cu[-1])
-    q_bits = _normal_bf16(st[1], (w.B, w.Hq, w.D))
+    q_bits = _normal_bf16(st[1], (w.B * w.n_q, w.Hq, w.D))
     ck, cv, chans, sk, sv = _channel_scales(w, st)
     shape = (ntok, w.Hkv, w.D)
     k_bits = _scaled_normal_bf16(st[2], shape, ck) if (ck != 1).any() else _normal_bf16(st[2], shape)
