@@ -40,6 +40,7 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   prm.n_q = a.n_q;
   prm.n_tiles = (a.n_q * prm.g + 15) / 16;
   prm.q_slot = (std::min(16, a.n_q * prm.g) * c.head_dim * 2 + 1023) / 1024 * 1024;
+  prm.wg_waves = std::min(prm.n_tiles, 4);              // several query tokens: tiles sharing a workgroup
   prm.ws_m = a.ws_m;
   prm.ws_l = a.ws_l;
   prm.ws_o = a.ws_o;
@@ -48,7 +49,8 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   prm.out = a.out;
   prm.err = a.err;
 
-  dim3 grid(a.n_chunks * prm.n_tiles, c.num_kv_heads);
+  const int groups = (prm.n_tiles + prm.wg_waves - 1) / prm.wg_waves;   // workgroups per (chunk, KV head)
+  dim3 grid(a.n_chunks * groups, c.num_kv_heads);
   hipError_t e;
   if (a.n_q > 1) e = launch_chunk_verify(prm, c.k_dtype, c.v_dtype, c.head_dim, grid, s);
   else e = (c.head_dim == 128) ? launch_kv<128, false>(c.k_dtype, c.v_dtype, prm, grid, s)

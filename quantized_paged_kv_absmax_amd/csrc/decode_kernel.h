@@ -84,6 +84,7 @@ struct Params {
   int32_t* err;
   int n_q;           // query tokens per sequence (1: decode; more: the last n_q positions, causally)
   int n_tiles;       // 16-column MFMA tiles of the n_q * g rows of a (sequence, KV head)
+  int wg_waves;      // several query tokens: waves (tiles) of a workgroup, which share its pages
 };
 
 // chunk kernels with several query tokens per sequence (verify.hip)
@@ -583,6 +584,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 32) (larger n: vmcnt(0))
+template <int N = 0>
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  if constexpr (N < 32) {
+    if (n == N) {
+      wait_vmcnt<N>();
+      return;
+    }
+    wait_vmcnt_rt<N + 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 template <int LPR, int NST>
 __device__ __forceinline__ void wait_rounds_after(int rounds_after) {
   // rounds_after in [0, NST-1]: the loads of that many later rounds may stay in flight
@@ -642,9 +657,14 @@ __device__ __forceinline__ int wave_incl_sum(int v) {
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 // MQ: several query tokens per sequence (verify); without it n_q is 1 and the
-// (token, head) row arithmetic folds away
+// (token, head) row arithmetic folds away.  With MQ a workgroup of up to four
+// waves, one per 16-column tile, shares each round: every wave DMAs a share of
+// the round's pages into the common LDS stage, waits for its share, and a
+// barrier makes the whole round visible; a second barrier after the round's
+// arithmetic frees the stage for the next DMA.  The page bytes are then read
+// once for all the tiles of a workgroup.
 template <int KT, int VT, int D, int CH, bool MQ>
-__global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
+__global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
   static_assert(CH <= kNp, "pages per round fit the descriptor");
   using KG = Geo<KT, D>;
@@ -679,7 +699,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // and the next segment sit in two dynamic-LDS buffers of p.q_slot bytes
   __shared__ __attribute__((aligned(16))) uint8_t lds0[SG::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[SG::STAGE];
-  extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t qlds_all[];
   auto stage_ptr = [&](auto s_tag) -> uint8_t* {
     if constexpr (decltype(s_tag)::value == 0) return lds0;
     else return lds1;
@@ -689,10 +709,14 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // chunk are neighbours in launch order, so they read its pages at about the
   // same time
   const int n_tiles = MQ ? p.n_tiles : 1;
-  const int tau = MQ ? (int)(blockIdx.x % n_tiles) : 0;
-  const int w = MQ ? (int)(blockIdx.x / n_tiles) : (int)blockIdx.x;
+  const int NW = MQ ? p.wg_waves : 1;                      // waves of the workgroup
+  const int wv = MQ ? (int)(threadIdx.x >> 6) : 0;         // this wave (its tile) in the workgroup
+  const int n_groups = (n_tiles + NW - 1) / NW;            // workgroups per (chunk, KV head)
+  const int tau = MQ ? (int)(blockIdx.x % n_groups) * NW + wv : 0;
+  const int w = MQ ? (int)(blockIdx.x / n_groups) : (int)blockIdx.x;
   const int kvh = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  uint8_t* qlds = qlds_all + 2 * p.q_slot * wv;            // this wave's two query buffers
   const int c = lane & 15, qg = lane >> 4;
   const int g = p.g;
   const int B = p.batch;
@@ -706,8 +730,9 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
 
   // warm the caches with the block table: each wave pulls one 256-byte slice of
   // it (into a ring stage not in use yet), so that the scalar loads of block ids
-  // after the length scan find their lines in L2 or the Infinity Cache
-  {
+  // after the length scan find their lines in L2 or the Infinity Cache.  Not with
+  // a shared ring: another wave's stage-1 DMA could land before this one.
+  if constexpr (!MQ) {
     const size_t bt_bytes = (size_t)B * p.max_blocks_per_seq * 4;
     const size_t off = ((size_t)kvh * gridDim.x + blockIdx.x) * 256;
     if (off < bt_bytes) {
@@ -797,7 +822,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   int wL = 0, wnp = 0, wex = 0, wlo = 0, whi = 0;
   int nwin = 0;
   bool more = false;
-  auto make_window = [&](bool from_regs) {
+  auto make_window = [&](bool from_regs) __attribute__((always_inline)) {
     const int sb = bs + lane;
     const bool wv = sb < B;
     if (from_regs) {
@@ -891,7 +916,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // ---- cursor over the rounds of the chunk (wave-uniform) ----
   int cj = -1, cpg = 0, clo = 0, chi = 0, cqb = kQBuf;
   int bad = 0;                                 // pages with an out-of-range block id
-  auto next = [&]() {
+  auto next = [&]() __attribute__((always_inline)) {
     Desc<CH> d;
     d.b = d.pg = d.L = d.info = 0;
 #pragma unroll
@@ -940,7 +965,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // segment, then K, V (and INT4 metadata) of its pages.  The ring waits count
   // only the page loads: loads issued before them are older, so a wait that
   // leaves the newest LPR loads in flight has finished them too.
-  auto issue = [&](const Desc<CH>& d, auto s_tag) {
+  auto issue = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
     uint8_t* sb = stage_ptr(s_tag);
     if (d.info & kFirst) {
       uint8_t* qd = qlds + ((d.info & kQBuf) ? p.q_slot : 0);
@@ -955,6 +980,10 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
         for (int t = 0; t < p.q_slot; t += 1024) dma16(rq, qd + t, t + 16 * lane);
       }
     }
+    // load unit u of the round (one DMA instruction) is this wave's when
+    // u % NW == wv (every unit when the wave is alone)
+    constexpr int UPP = KP::NINSTR + VP::NINSTR + (SG::META ? 2 : 0);   // units per page
+    auto mine = [&](int u) { return !MQ || u % NW == wv; };
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const bool ok = d.bid[i] >= 0;
@@ -963,16 +992,18 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       const uint64_t voffb = (VPAGE == KPAGE) ? koffb : (uint64_t)bid * vstride;
       const auto rk = page_rsrc(kbase + koffb, ok ? KPAGE : 0);
 #pragma unroll
-      for (int t = 0; t < KP::NINSTR; ++t) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
+      for (int t = 0; t < KP::NINSTR; ++t)
+        if (mine(i * UPP + t)) dma16(rk, sb + SG::K_OFF + i * KP::SLOT + 1024 * t, koff[t]);
       const auto rv = page_rsrc(vbase + voffb, ok ? VPAGE : 0);
 #pragma unroll
-      for (int t = 0; t < VP::NINSTR; ++t) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
+      for (int t = 0; t < VP::NINSTR; ++t)
+        if (mine(i * UPP + KP::NINSTR + t)) dma16(rv, sb + SG::V_OFF + i * VP::SLOT + 1024 * t, voff[t]);
       if constexpr (SG::META) {
         const uint64_t moff = (uint64_t)bid * mstride;
         const auto rkm = page_rsrc(reinterpret_cast<const uint8_t*>(kmbase) + moff, ok ? 128 : 0);
-        dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
+        if (mine(i * UPP + KP::NINSTR + VP::NINSTR)) dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
         const auto rvm = page_rsrc(reinterpret_cast<const uint8_t*>(vmbase) + moff, ok ? 128 : 0);
-        dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
+        if (mine(i * UPP + KP::NINSTR + VP::NINSTR + 1)) dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
       }
     }
   };
@@ -1005,7 +1036,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // L - n_q + i + 1 (decode: L)
   const int lim_off = MQ ? 1 - n_q + (hv_lane ? (col0 + c) / g : 0) : 0;
 
-  auto begin_segment = [&](const Desc<CH>& d) {
+  auto begin_segment = [&](const Desc<CH>& d) __attribute__((always_inline)) {
     m_ref = -INFINITY;
     corr_run = 0.0f;
     l_run = 0.0f;
@@ -1119,7 +1150,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // ---- one round from an LDS stage: QK, softmax, PV ----
   // TAIL: the round holds the sequence's last page, the only one with tokens past
   // its end; other rounds skip every per-token test.
-  auto round = [&](auto tail_tag, const Desc<CH>& cur, auto s_tag) {
+  auto round = [&](auto tail_tag, const Desc<CH>& cur, auto s_tag) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const uint8_t* sb = stage_ptr(s_tag);
 
@@ -1353,7 +1384,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   };
 
   // ---- end of a segment: the sequence's output, or the piece's partial ----
-  auto end_segment = [&](const Desc<CH>& d) {
+  auto end_segment = [&](const Desc<CH>& d) __attribute__((always_inline)) {
     float c_all = 0.0f, l_all = 0.0f;
     if constexpr (VT == DT_INT4) {
       c_all = xor32_sum(xor16_sum(corr_run));
@@ -1428,7 +1459,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
     else __builtin_amdgcn_s_setprio(0);
     ++done_rounds;
   };
-  auto compute = [&](const Desc<CH>& d, auto s_tag) {
+  auto compute = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
     pace();
     if (d.info & kFirst) begin_segment(d);
     if (d.info & kTail) round(std::true_type{}, d, s_tag);
@@ -1444,14 +1475,20 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
   // query-row loads when it opens a segment; a fixed LPR would make the wave
   // wait for part of d itself, one full memory latency at every segment start
   const int nq = p.q_slot >> 10;              // query-row loads of a segment (1 to 4)
+  // a workgroup's wave issues every NW-th load unit of a round
+  const int my_lpr = (SG::LPR - wv + NW - 1) / NW;
   auto wait_issued = [&](const Desc<CH>& d) {
     if (!(d.info & kNp)) wait_vmcnt<0>();
+    else if (MQ) wait_vmcnt_rt(my_lpr + ((d.info & kFirst) ? nq : 0));
     else if (!(d.info & kFirst)) wait_vmcnt<SG::LPR>();
     else if (nq <= 1) wait_vmcnt<SG::LPR + 1>();
     else if (nq == 2) wait_vmcnt<SG::LPR + 2>();
     else if (nq == 3) wait_vmcnt<SG::LPR + 3>();
     else wait_vmcnt<SG::LPR + 4>();
   };
+  // With MQ the waves of the workgroup share each round: a barrier after every
+  // wave's wait for its share makes the round visible to all, and a barrier
+  // after the round's arithmetic frees its stage for the next DMA.
   Desc<CH> da = next();
   if (da.info & kNp) {
     Desc<CH> dn = next();
@@ -1462,14 +1499,18 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(Params p) {
       db = dn;
       dn = next();
       wait_issued(db);
+      if constexpr (MQ) __builtin_amdgcn_s_barrier();
       compute(da, S0{});
+      if constexpr (MQ) __builtin_amdgcn_s_barrier();
       if (!(db.info & kNp)) break;
 
       if (dn.info & kNp) issue(dn, S0{});
       da = dn;
       dn = next();
       wait_issued(da);
+      if constexpr (MQ) __builtin_amdgcn_s_barrier();
       compute(db, S1{});
+      if constexpr (MQ) __builtin_amdgcn_s_barrier();
       if (!(da.info & kNp)) break;
     }
   }
@@ -1488,8 +1529,9 @@ constexpr int pages_per_round() {
 
 template <int KT, int VT, int D, bool MQ>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, pages_per_round<KT, VT>(), MQ>), grid, dim3(64),
-                     2 * prm.q_slot, s, prm);
+  const int nw = MQ ? prm.wg_waves : 1;
+  hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, pages_per_round<KT, VT>(), MQ>), grid, dim3(64 * nw),
+                     2 * prm.q_slot * nw, s, prm);
   return hipGetLastError();
 }
 
