@@ -1150,7 +1150,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // ---- one round from an LDS stage: QK, softmax, PV ----
   // TAIL: the round holds the sequence's last page, the only one with tokens past
   // its end; other rounds skip every per-token test.
-  auto round = [&](auto tail_tag, const Desc<CH>& cur, auto s_tag) __attribute__((always_inline)) {
+  auto round = [&](auto tail_tag, const Desc<CH>& cur, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const uint8_t* sb = stage_ptr(s_tag);
 
@@ -1212,6 +1212,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
       if constexpr (KT == DT_INT4) { lds_tie(km[i][0]); lds_tie(km[i][1]); }
       if constexpr (VT == DT_INT4) { lds_tie(vm[i][0]); lds_tie(vm[i][1]); }
     }
+    after_reads();   // the stage's data is in registers: the stage may be refilled
 
     // QK: logits of head c for tokens 4qg+r of each page
     float sl[CH][4];
@@ -1459,11 +1460,11 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     else __builtin_amdgcn_s_setprio(0);
     ++done_rounds;
   };
-  auto compute = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
+  auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
     pace();
     if (d.info & kFirst) begin_segment(d);
-    if (d.info & kTail) round(std::true_type{}, d, s_tag);
-    else round(std::false_type{}, d, s_tag);
+    if (d.info & kTail) round(std::true_type{}, d, s_tag, after_reads);
+    else round(std::false_type{}, d, s_tag, after_reads);
     if (d.info & kLast) end_segment(d);
   };
 
@@ -1486,32 +1487,68 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     else if (nq == 3) wait_vmcnt<SG::LPR + 3>();
     else wait_vmcnt<SG::LPR + 4>();
   };
-  // With MQ the waves of the workgroup share each round: a barrier after every
-  // wave's wait for its share makes the round visible to all, and a barrier
-  // after the round's arithmetic frees its stage for the next DMA.
+  // Several query tokens: the waves of the workgroup share each round, so a
+  // barrier after every wave's wait for its share makes the round visible to
+  // all, and a barrier after every wave has read it frees its stage.
+  // kEarly: both stages are filled at the start, and the round after next is
+  // issued into a stage as soon as the barrier marks it read, ahead of the
+  // round's arithmetic, so it has nearly two rounds of arithmetic to arrive in.
+  // With a bf16 V operand the registers this keeps live push the kernel past
+  // 256 VGPRs (one wave per SIMD), so there, as with one query token, the
+  // round after next is issued once the round is done.
+  constexpr bool kEarly = MQ && VT != DT_BF16;
   Desc<CH> da = next();
-  if (da.info & kNp) {
-    Desc<CH> dn = next();
-    Desc<CH> db;
-    issue(da, S0{});
-    while (true) {
-      if (dn.info & kNp) issue(dn, S1{});
-      db = dn;
-      dn = next();
-      wait_issued(db);
-      if constexpr (MQ) __builtin_amdgcn_s_barrier();
-      compute(da, S0{});
-      if constexpr (MQ) __builtin_amdgcn_s_barrier();
-      if (!(db.info & kNp)) break;
+  if constexpr (!kEarly) {
+    if (da.info & kNp) {
+      Desc<CH> dn = next();
+      Desc<CH> db;
+      auto none = []() __attribute__((always_inline)) {};
+      issue(da, S0{});
+      while (true) {
+        if (dn.info & kNp) issue(dn, S1{});
+        db = dn;
+        dn = next();
+        wait_issued(db);
+        if constexpr (MQ) __builtin_amdgcn_s_barrier();
+        compute(da, S0{}, none);
+        if constexpr (MQ) __builtin_amdgcn_s_barrier();
+        if (!(db.info & kNp)) break;
 
-      if (dn.info & kNp) issue(dn, S0{});
+        if (dn.info & kNp) issue(dn, S0{});
+        da = dn;
+        dn = next();
+        wait_issued(da);
+        if constexpr (MQ) __builtin_amdgcn_s_barrier();
+        compute(db, S1{}, none);
+        if constexpr (MQ) __builtin_amdgcn_s_barrier();
+        if (!(da.info & kNp)) break;
+      }
+    }
+  } else if (da.info & kNp) {
+    Desc<CH> db = next();
+    issue(da, S0{});
+    if (db.info & kNp) issue(db, S1{});
+    Desc<CH> dn = next();
+    while (true) {
+      wait_issued(db);
+      __builtin_amdgcn_s_barrier();
+      compute(da, S0{}, [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_barrier();
+        if (dn.info & kNp) issue(dn, S0{});
+      });
+      if (!(db.info & kNp)) break;
       da = dn;
       dn = next();
+
       wait_issued(da);
-      if constexpr (MQ) __builtin_amdgcn_s_barrier();
-      compute(db, S1{});
-      if constexpr (MQ) __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+      compute(db, S1{}, [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_barrier();
+        if (dn.info & kNp) issue(dn, S1{});
+      });
       if (!(da.info & kNp)) break;
+      db = dn;
+      dn = next();
     }
   }
   if (bad && p.err && lane == 0) atomicAdd(p.err, bad);
