@@ -56,11 +56,24 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   else e = (c.head_dim == 128) ? launch_kv<128, false>(c.k_dtype, c.v_dtype, prm, grid, s)
                                : launch_kv<64, false>(c.k_dtype, c.v_dtype, prm, grid, s);
   if (e != hipSuccess || a.ws_rec == nullptr) return e;
-  dim3 rgrid(a.num_q_heads * a.n_q, a.batch);
-  if (c.head_dim == 128)
-    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kRedThreads), 0, s, prm);
-  else
-    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kRedThreads), 0, s, prm);
+  // many rows with few pieces each (several query tokens, a large batch): a lane
+  // group per row; else a workgroup per row, its groups splitting the pieces
+  const int64_t rows = (int64_t)a.num_q_heads * a.n_q;
+  const bool by_rows = rows * a.batch >= 8192 && a.n_chunks <= 3 * a.batch;
+  if (by_rows) {
+    const int per_block = kRedThreads / (c.head_dim / 4);
+    dim3 rgrid((unsigned)((rows + per_block - 1) / per_block), a.batch);
+    if (c.head_dim == 128)
+      hipLaunchKernelGGL(decode_reduce_rows_kernel<128>, rgrid, dim3(kRedThreads), 0, s, prm);
+    else
+      hipLaunchKernelGGL(decode_reduce_rows_kernel<64>, rgrid, dim3(kRedThreads), 0, s, prm);
+  } else {
+    dim3 rgrid((unsigned)rows, a.batch);
+    if (c.head_dim == 128)
+      hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kRedThreads), 0, s, prm);
+    else
+      hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kRedThreads), 0, s, prm);
+  }
   return hipGetLastError();
 }
 

@@ -393,16 +393,70 @@ __device__ __forceinline__ void buf_load_v_row(uint32_t (&r)[N], __amdgpu_buffer
 }
 
 // ---------------------------------------------------------------------------
-// split-KV reduce: one workgroup per (query head, sequence) merges the pieces of
-// a sequence that chunk boundaries cut:
+// split-KV reduce: merges the pieces of a sequence that chunk boundaries cut,
 //   o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j.
-// Piece j of sequence b (chunk rec.x + j) sits in slot rec.x + j + b.  Lane
-// groups of D/4 lanes (4 columns each) take every NG-th piece with a running
-// maximum, and LDS combines the groups.  A separate launch: the kernel boundary
-// makes every piece's stores visible without a device-wide fence.
+// Piece j of sequence b (chunk rec.x + j) sits in slot rec.x + j + b.  A lane
+// group of D/4 lanes holds one row's 4-column slices.  A separate launch: the
+// kernel boundary makes every piece's stores visible without a device-wide
+// fence.
+//   decode_reduce_kernel: one workgroup per (row, sequence); its groups take
+//     every NG-th piece, and LDS combines the groups (for few rows with many
+//     pieces each: a long context cut into hundreds of chunks).
+//   decode_reduce_rows_kernel: one group per row, NG rows of a sequence per
+//     workgroup (for many rows with few pieces each: several query tokens).
 // ---------------------------------------------------------------------------
 
 constexpr int kRedThreads = 256;
+
+// running merge of pieces (m_j, l_j, acc_j) for one lane's 4 columns
+struct PieceMerge {
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  __device__ __forceinline__ void add(float mj, float lj, const float4& v) {
+    const bool ok = (mj != -INFINITY);        // -inf: past P, or a piece with no valid token
+    const float Mn = ok ? fmaxf(M, mj) : M;
+    const float sc = (Mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float f = ok ? __builtin_amdgcn_exp2f(mj - Mn) : 0.0f;
+    acc.x = acc.x * sc + (ok ? f * v.x : 0.0f);
+    acc.y = acc.y * sc + (ok ? f * v.y : 0.0f);
+    acc.z = acc.z * sc + (ok ? f * v.z : 0.0f);
+    acc.w = acc.w * sc + (ok ? f * v.w : 0.0f);
+    den = den * sc + (ok ? f * lj : 0.0f);
+    M = Mn;
+  }
+};
+
+// pieces j0, j0 + step, ... (U of them, those past P masked) of one row, all
+// loads in flight before any is used
+template <int U, int D>
+__device__ __forceinline__ void merge_pieces(PieceMerge& pm, const float* m, const float* l, const float* o,
+                                             int RS, int P, int j0, int step, int ln) {
+  float mj[U], lj[U];
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + u * step;
+    const size_t jj = (size_t)min(j, P - 1);
+    mj[u] = (j < P) ? m[jj * RS] : -INFINITY;
+    lj[u] = l[jj * RS];
+    v[u] = *reinterpret_cast<const float4*>(o + jj * RS * D + 4 * ln);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) pm.add(mj[u], lj[u], v[u]);
+}
+
+// the normalised row slice (zeros when no piece holds a valid token)
+__device__ __forceinline__ void store_row_slice(const Params& p, size_t oi, float4 a, float dd) {
+  const bool any = dd > 0.0f;
+  const float r[4] = {any ? a.x / dd : 0.0f, any ? a.y / dd : 0.0f, any ? a.z / dd : 0.0f, any ? a.w / dd : 0.0f};
+  if (p.out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
+  } else {
+    const uint32_t lo = (uint32_t)f32_to_bf16_bits(r[0]) | ((uint32_t)f32_to_bf16_bits(r[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_bits(r[2]) | ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + oi) = make_uint2(lo, hi);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
@@ -425,51 +479,21 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
   const float* o = wo + (s0 * RS + hq) * D;
 
   const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
-  float M = -INFINITY, den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto combine = [&](float mj, float lj, const float4& v) {
-    const bool ok = (mj != -INFINITY);        // -inf: past P, or a piece with no valid token
-    const float Mn = ok ? fmaxf(M, mj) : M;
-    const float sc = (Mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-    const float f = ok ? __builtin_amdgcn_exp2f(mj - Mn) : 0.0f;
-    acc.x = acc.x * sc + (ok ? f * v.x : 0.0f);
-    acc.y = acc.y * sc + (ok ? f * v.y : 0.0f);
-    acc.z = acc.z * sc + (ok ? f * v.z : 0.0f);
-    acc.w = acc.w * sc + (ok ? f * v.w : 0.0f);
-    den = den * sc + (ok ? f * lj : 0.0f);
-    M = Mn;
-  };
+  PieceMerge pm;
   if (P <= NG) {
     // at most one piece per group (branch-free, so the three loads go out together)
-    const size_t jj = (size_t)min(grp, P - 1);
-    const float mj = (grp < P) ? m[jj * RS] : -INFINITY;
-    const float lj = l[jj * RS];
-    const float4 v = *reinterpret_cast<const float4*>(o + jj * RS * D + 4 * ln);
-    combine(mj, lj, v);
+    merge_pieces<1, D>(pm, m, l, o, RS, P, grp, NG, ln);
   } else {
-    // eight pieces per group and pass, their loads all in flight before any is
-    // used: a sequence cut into hundreds of pieces is then a few round trips
-    for (int j0 = grp; j0 < P; j0 += 8 * NG) {
-      float mj[8], lj[8];
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u * NG;
-        const size_t jj = (size_t)min(j, P - 1);
-        mj[u] = (j < P) ? m[jj * RS] : -INFINITY;
-        lj[u] = l[jj * RS];
-        v[u] = *reinterpret_cast<const float4*>(o + jj * RS * D + 4 * ln);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) combine(mj[u], lj[u], v[u]);
-    }
+    // eight pieces per group and pass: a sequence cut into hundreds of pieces
+    // is then a few round trips
+    for (int j0 = grp; j0 < P; j0 += 8 * NG) merge_pieces<8, D>(pm, m, l, o, RS, P, j0, NG, ln);
   }
   __shared__ float4 s_acc[NG][LPG];
   __shared__ float s_m[NG], s_den[NG];
-  s_acc[grp][ln] = acc;
+  s_acc[grp][ln] = pm.acc;
   if (ln == 0) {
-    s_m[grp] = M;
-    s_den[grp] = den;
+    s_m[grp] = pm.M;
+    s_den[grp] = pm.den;
   }
   __syncthreads();
   if (threadIdx.x < LPG) {
@@ -485,17 +509,33 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(Params p) {
       a.x += f * v.x; a.y += f * v.y; a.z += f * v.z; a.w += f * v.w;
       dd += f * s_den[gi];
     }
-    const bool any = dd > 0.0f;                 // no valid token at all: zeros
-    const float r[4] = {any ? a.x / dd : 0.0f, any ? a.y / dd : 0.0f, any ? a.z / dd : 0.0f, any ? a.w / dd : 0.0f};
-    const size_t oi = ((size_t)b * RS + hq) * D + 4 * threadIdx.x;
-    if (p.out_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
-    } else {
-      const uint32_t lo = (uint32_t)f32_to_bf16_bits(r[0]) | ((uint32_t)f32_to_bf16_bits(r[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_bits(r[2]) | ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + oi) = make_uint2(lo, hi);
-    }
+    store_row_slice(p, ((size_t)b * RS + hq) * D + 4 * threadIdx.x, a, dd);
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRedThreads) void decode_reduce_rows_kernel(Params p) {
+  constexpr int LPG = D / 4;                  // lanes per group
+  constexpr int NG = kRedThreads / LPG;       // rows per workgroup
+  const float* wm = p.ws_m;
+  const float* wl = p.ws_l;
+  const float* wo = p.ws_o;
+  const int RS = p.Hq * p.n_q;                // rows per sequence and slot
+  asm volatile("" ::"s"(wm), "s"(wl), "s"(wo), "s"(RS));
+  const int b = blockIdx.y;
+  const int2 rec = p.ws_rec[b];
+  if (rec.y <= rec.x) return;                 // one piece: the chunk kernel wrote the rows
+  const int grp = threadIdx.x / LPG, ln = threadIdx.x % LPG;
+  const int hq = blockIdx.x * NG + grp;
+  if (hq >= RS) return;
+  const int P = rec.y - rec.x + 1;
+  const size_t s0 = (size_t)rec.x + b;
+  const float* m = wm + s0 * RS + hq;
+  const float* l = wl + s0 * RS + hq;
+  const float* o = wo + (s0 * RS + hq) * D;
+  PieceMerge pm;
+  for (int j0 = 0; j0 < P; j0 += 4) merge_pieces<4, D>(pm, m, l, o, RS, P, j0, 1, ln);
+  store_row_slice(p, ((size_t)b * RS + hq) * D + 4 * ln, pm.acc, pm.den);
 }
 
 // ---------------------------------------------------------------------------

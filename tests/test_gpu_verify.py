@@ -96,3 +96,28 @@ def test_verify16_workload_reduced():
         mx, bad = gate_errors(out, ref, "bf16")
         log(f"[verify16_int8 B=6] partition={part} max|err|={mx:.3e}")
         assert bad == 0
+
+
+# many (token, head) rows with few pieces each: the reduce takes one lane group
+# per row, workgroups of 8 (D = 128) or 16 (D = 64) rows; the second case leaves
+# a partly filled workgroup (138 rows a sequence) and sequences shorter than n_q
+ROW_CASES = [
+    ("int8", "int8", 32, 8, 128, 16, 24, (1, 700)),
+    ("e4m3", "e5m2", 6, 2, 64, 23, 72, (1, 200)),
+]
+
+
+@pytest.mark.parametrize("kd,vd,Hq,Hkv,D,n_q,B,lens", ROW_CASES)
+def test_verify_many_rows(kd, vd, Hq, Hkv, D, n_q, B, lens):
+    w = WORKLOADS["tiny_int8"].with_(B=B, lens=("uniform",) + lens, Hq=Hq, Hkv=Hkv, D=D, k_dtype=kd, v_dtype=vd,
+                                     seed=41, n_q=n_q, new_tokens=0, calib="all")
+    inp = make_decode_inputs(w)
+    r = build_library_cache(w, inp)
+    o = build_oracle_cache(w, inp)
+    ref = oracle_decode(o, inp)
+    for odt in ("f32", "bf16"):
+        out = library_decode(r, inp, partition=0, out_dtype=odt)
+        torch.cuda.synchronize()
+        mx, bad = gate_errors(out, ref, odt)
+        log(f"[verify rows {kd}/{vd} B={B} n_q={n_q} Hq={Hq} D={D}] out={odt} max|err|={mx:.3e}")
+        assert bad == 0
