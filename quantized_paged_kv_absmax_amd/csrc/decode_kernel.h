@@ -750,7 +750,8 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // same time
   const int n_tiles = MQ ? p.n_tiles : 1;
   const int NW = MQ ? p.wg_waves : 1;                      // waves of the workgroup
-  const int wv = MQ ? (int)(threadIdx.x >> 6) : 0;         // this wave (its tile) in the workgroup
+  // this wave (its tile) in the workgroup, wave-uniform (a scalar register)
+  const int wv = MQ ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const int n_groups = (n_tiles + NW - 1) / NW;            // workgroups per (chunk, KV head)
   const int tau = MQ ? (int)(blockIdx.x % n_groups) * NW + wv : 0;
   const int w = MQ ? (int)(blockIdx.x / n_groups) : (int)blockIdx.x;
@@ -945,13 +946,23 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // row (token i, head h) of the sequence's query block; pieces of columns past
   // the rows read from beyond the buffer's range, as zeros
   const int q_bytes = n_q * p.Hq * D * 2;        // one sequence's query block
-  auto q_piece_offset = [&](int t) {
+  int q_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
     const int piece = 64 * t + lane;
     const int cc = piece / (D / 8), within = 16 * (piece % (D / 8));
     const int r = col0 + cc;
-    if (cc >= 16 || r >= rows) return q_bytes;
-    return ((r / g) * p.Hq + kvh * g + r % g) * D * 2 + within;
-  };
+    const int off = ((r / g) * p.Hq + kvh * g + r % g) * D * 2 + within;
+    q_off[t] = (MQ && cc < 16 && r < rows) ? off : q_bytes;
+  }
+
+  const int nq = p.q_slot >> 10;              // query-row loads of a segment (1 to 4)
+  // DMA units of a round: one instruction each, K, V (and INT4 metadata) of
+  // each page in turn; with several waves, unit u is wave (u % NW)'s
+  constexpr int UPP = KP::NINSTR + VP::NINSTR + (SG::META ? 2 : 0);   // units per page
+  static_assert(CH * UPP <= 32, "DMA units of a round");
+  uint32_t my_units = 0;
+  for (int u = 0; u < CH * UPP; ++u) my_units |= (u % NW == wv) ? (1u << u) : 0u;
 
   // ---- cursor over the rounds of the chunk (wave-uniform) ----
   int cj = -1, cpg = 0, clo = 0, chi = 0, cqb = kQBuf;
@@ -1007,23 +1018,26 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // leaves the newest LPR loads in flight has finished them too.
   auto issue = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
     uint8_t* sb = stage_ptr(s_tag);
+    // the per-unit tests below are scalar bit tests made here, each time: hoisted
+    // out of the loop as lane masks they would crowd the scalar registers
+    const uint32_t mu = MQ ? (uint32_t)__builtin_amdgcn_readfirstlane((int)my_units) : ~0u;
+    const int nqo = MQ ? __builtin_amdgcn_readfirstlane(nq) : nq;
     if (d.info & kFirst) {
       uint8_t* qd = qlds + ((d.info & kQBuf) ? p.q_slot : 0);
       if constexpr (MQ) {
         const auto rq = page_rsrc(p.q + (size_t)d.b * n_q * p.Hq * D, q_bytes);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (1024 * t < p.q_slot) dma16(rq, qd + 1024 * t, q_piece_offset(t));
+          if (t < nqo) dma16(rq, qd + 1024 * t, q_off[t]);
       } else {
         // one token: its g rows are one contiguous run
         const auto rq = page_rsrc(p.q + ((size_t)d.b * p.Hq + (size_t)kvh * g) * D, g * D * 2);
         for (int t = 0; t < p.q_slot; t += 1024) dma16(rq, qd + t, t + 16 * lane);
       }
     }
-    // load unit u of the round (one DMA instruction) is this wave's when
-    // u % NW == wv (every unit when the wave is alone)
-    constexpr int UPP = KP::NINSTR + VP::NINSTR + (SG::META ? 2 : 0);   // units per page
-    auto mine = [&](int u) { return !MQ || u % NW == wv; };
+    // load unit u of the round (one DMA instruction) is this wave's when bit u
+    // of my_units is set (every unit when the wave is alone)
+    auto mine = [&](int u) { return !MQ || ((mu >> u) & 1u); };
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const bool ok = d.bid[i] >= 0;
@@ -1515,7 +1529,6 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // wait for everything but the round just issued (d): its page loads, plus its
   // query-row loads when it opens a segment; a fixed LPR would make the wave
   // wait for part of d itself, one full memory latency at every segment start
-  const int nq = p.q_slot >> 10;              // query-row loads of a segment (1 to 4)
   // a workgroup's wave issues every NW-th load unit of a round
   const int my_lpr = (SG::LPR - wv + NW - 1) / NW;
   auto wait_issued = [&](const Desc<CH>& d) {
