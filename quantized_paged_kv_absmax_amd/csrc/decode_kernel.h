@@ -1504,18 +1504,18 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // rest of the kernel with half its waves.  Each wave lowers its own priority
   // as its share of the chunk gets done, so the one that is behind is served
   // first and the waves of a CU finish together.
-  int done_rounds = 0;
+  // (the quarter of the chunk done, 4 done / total, by comparisons, not a division)
+  int done4 = 0;
   const int total_rounds = max(1, (x1 - x0 + CH - 1) / CH);
   auto pace = [&]() {
-    const int q = (4 * done_rounds) / total_rounds;
-    if (q <= 0) __builtin_amdgcn_s_setprio(3);
-    else if (q == 1) __builtin_amdgcn_s_setprio(2);
-    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    if (done4 < total_rounds) __builtin_amdgcn_s_setprio(3);
+    else if (done4 < 2 * total_rounds) __builtin_amdgcn_s_setprio(2);
+    else if (done4 < 3 * total_rounds) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
-    ++done_rounds;
+    done4 += 4;
   };
   auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
-    pace();
+    if constexpr (!MQ) pace();   // the workgroup's barriers already keep its waves together
     if (d.info & kFirst) begin_segment(d);
     if (d.info & kTail) round(std::true_type{}, d, s_tag, after_reads);
     else round(std::false_type{}, d, s_tag, after_reads);
