@@ -71,11 +71,24 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
   *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
 }
 
+// this lane's 16 source bytes of a row, and the row's scale
+struct RowIn {
+  uint4 raw;
+  float s;
+};
+
 template <int D>
-__device__ __forceinline__ void process_row(const RowSide& sd, const uint16_t* src_row, int64_t dst_row_idx,
-                                            int h, int j) {
+__device__ __forceinline__ RowIn load_row(const RowSide& sd, const uint16_t* src_row, int h, int j) {
+  RowIn in;
+  in.raw = *reinterpret_cast<const uint4*>(src_row + 8 * j);
+  in.s = sd.scale ? sd.scale[sd.scale_per_head ? h : 0] : 1.0f;
+  return in;
+}
+
+template <int D>
+__device__ __forceinline__ void store_row(const RowSide& sd, const RowIn& in, int64_t dst_row_idx, int j) {
   constexpr int LPR = D / 8;
-  const uint4 raw = *reinterpret_cast<const uint4*>(src_row + 8 * j);
+  const uint4 raw = in.raw;
   if (sd.dtype == DT_BF16) {
     *reinterpret_cast<uint4*>(sd.pages + dst_row_idx * (2 * D) + 16 * j) = raw;
     return;
@@ -87,14 +100,13 @@ __device__ __forceinline__ void process_row(const RowSide& sd, const uint16_t* s
     x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
     x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
   }
-  float s = 1.0f;
-  if (sd.scale) s = sd.scale[sd.scale_per_head ? h : 0];
   const int rb = (sd.dtype == DT_INT4) ? D / 2 : D;
-  encode_store<D, LPR>(x, sd.dtype, s, sd.pages + dst_row_idx * rb,
+  encode_store<D, LPR>(x, sd.dtype, in.s, sd.pages + dst_row_idx * rb,
                        sd.meta ? sd.meta + dst_row_idx * 2 : nullptr, j);
 }
 
-template <int D>
+// R32: the row count fits 31 bits, so (token, head) come from a 32-bit division
+template <int D, bool R32>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSide v, const int64_t* slots,
                                                                int64_t T, int Hkv, int64_t num_slots,
                                                                int32_t* err) {
@@ -104,8 +116,18 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSid
   const int j = threadIdx.x % LPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   if (row >= T * Hkv) return;
-  const int64_t t = row / Hkv;
-  const int h = (int)(row % Hkv);
+  int64_t t;
+  int h;
+  if constexpr (R32) {
+    t = (int64_t)((uint32_t)row / (uint32_t)Hkv);
+    h = (int)((uint32_t)row - (uint32_t)t * (uint32_t)Hkv);
+  } else {
+    t = row / Hkv;
+    h = (int)(row % Hkv);
+  }
+  // the row's loads go out together with the slot's: one memory round trip
+  // before the store, not two
+  const RowIn in = load_row<D>(sd, sd.src + row * D, h, j);
   const int64_t slot = slots[t];
   if (slot < 0) return;
   if (slot >= num_slots) {
@@ -114,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSid
   }
   const int64_t blk = slot / 16, off = slot % 16;
   const int64_t dst = (blk * Hkv + h) * 16 + off;
-  process_row<D>(sd, sd.src + row * D, dst, h, j);
+  store_row<D>(sd, in, dst, j);
 }
 
 template <int D>
@@ -128,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v,
   if (r >= (int64_t)n_blocks * Hkv * 16) return;
   const int64_t dst = (int64_t)first_block * Hkv * 16 + r;          // same slot in source and dest
   const int h = (int)((dst / 16) % Hkv);
-  process_row<D>(sd, sd.src + dst * D, dst, h, j);
+  store_row<D>(sd, load_row<D>(sd, sd.src + dst * D, h, j), dst, j);
 }
 
 RowSide side(const CacheView& c, bool is_k, const uint16_t* src) {
@@ -150,14 +172,23 @@ hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const u
   const RowSide k = side(c, true, k_new), v = side(c, false, v_new);
   const int64_t rows = T * c.num_kv_heads;
   const int64_t num_slots = (int64_t)c.num_blocks * 16;
+  const bool r32 = rows <= 0x7fffffff;
   if (c.head_dim == 128) {
     dim3 grid((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)), 2);
-    hipLaunchKernelGGL(cache_write_kernel<128>, grid, dim3(kThreads), 0, s, k, v, slots, T, c.num_kv_heads,
-                       num_slots, err);
+    if (r32)
+      hipLaunchKernelGGL((cache_write_kernel<128, true>), grid, dim3(kThreads), 0, s, k, v, slots, T,
+                         c.num_kv_heads, num_slots, err);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<128, false>), grid, dim3(kThreads), 0, s, k, v, slots, T,
+                         c.num_kv_heads, num_slots, err);
   } else {
     dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)), 2);
-    hipLaunchKernelGGL(cache_write_kernel<64>, grid, dim3(kThreads), 0, s, k, v, slots, T, c.num_kv_heads,
-                       num_slots, err);
+    if (r32)
+      hipLaunchKernelGGL((cache_write_kernel<64, true>), grid, dim3(kThreads), 0, s, k, v, slots, T,
+                         c.num_kv_heads, num_slots, err);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<64, false>), grid, dim3(kThreads), 0, s, k, v, slots, T,
+                         c.num_kv_heads, num_slots, err);
   }
   return hipGetLastError();
 }
