@@ -351,6 +351,19 @@ __device__ __forceinline__ float unpack_hi(uint32_t v, bool bf) {
   return (float)__builtin_bit_cast(f16x2, v)[1];
 }
 
+// fp16 pair of the remainders (a - h.lo, b - h.hi), h the fp16 pair of (a, b):
+// each remainder is exact in fp32 (h is a rounded to 11 bits), so one mixed
+// fma per element, reading its half of h as fp16, gives the same bits as
+// converting h back, subtracting and packing
+__device__ __forceinline__ uint32_t f16_remainders(float a, float b, uint32_t h) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(r)
+      : "v"(h), "v"(a), "v"(b));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // per-page buffer resources: a page's K (or V, or INT4 metadata) rows form one
 // contiguous range; a descriptor covering exactly that range (0 bytes for an
@@ -1405,9 +1418,12 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         }
         aop[2 * h2] = a0;
         aop[2 * h2 + 1] = a1;
-        if constexpr (VT != DT_INT4 && (WBF || WSPLIT)) {
-          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, WBF), pr[1] - unpack_hi(a0, WBF), WBF);
-          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, WBF), pr[3] - unpack_hi(a1, WBF), WBF);
+        if constexpr (VT != DT_INT4 && WBF) {
+          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
+          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
+        } else if constexpr (VT != DT_INT4 && WSPLIT) {
+          aop_lo[2 * h2] = f16_remainders(pr[0], pr[1], a0);
+          aop_lo[2 * h2 + 1] = f16_remainders(pr[2], pr[3], a1);
         }
 
         v_operands<VT, D>(vw, vop[h2]);
