@@ -225,9 +225,11 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
  * tokens: token i (row b * n_q + i of q and out) sits at position
  * p = seq_lens[b] - n_q + i and attends to cache positions 0..p; p < 0 gives a
  * zero row.  Per KV head, the n_q * g (query token, head) rows run as tiles of
- * 16 MFMA columns, one wave per (chunk, KV head, tile); the work split, the
- * workspace and the reduce are those of kvq_paged_attention_decode, which is
- * this call with n_q = 1.
+ * 16 MFMA columns, a wave per tile; the tiles of a (chunk, KV head), up to four
+ * at a time, form one workgroup that reads each page from memory once.  The work
+ * split, the workspace and the reduce are those of kvq_paged_attention_decode,
+ * which is this call with n_q = 1, except that partition = 0 makes about
+ * 2048 / (num_kv_heads * tiles) chunks.
  *   q      (device) bf16 [batch * n_q][num_q_heads][head_dim], token-major
  *   n_q    >= 1, n_q * num_q_heads <= 65535
  *   out    (device) [batch * n_q][num_q_heads][head_dim] of out_dtype
