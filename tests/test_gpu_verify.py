@@ -26,13 +26,15 @@ def _small(kd, vd, Hq, Hkv, D, n_q, lens, seed=31):
 
 
 # (K, V, Hq, Hkv, D, n_q): g = 4 with 16 tokens (4 tiles), g = 3 (a token's heads
-# cut by a tile edge), g = 8 with odd n_q, g = 16 (one token per tile), g = 1
+# cut by a tile edge), g = 8 with odd n_q, g = 16 (one token per tile), g = 1,
+# and 64 tokens
 CASES = [
     ("int8", "int8", 8, 2, 128, 16),
     ("e4m3", "e5m2", 6, 2, 128, 7),
     ("int4", "int4", 16, 2, 128, 5),
     ("bf16", "bf16", 16, 1, 64, 3),
     ("e4m3", "int8", 2, 2, 64, 20),
+    ("int8", "e4m3", 8, 2, 128, 64),      # a prefill chunk: 16 tiles, 4 workgroups per (chunk, KV head)
 ]
 
 
