@@ -48,10 +48,11 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
     float sc = (mx - mn) / 15.0f;
     if (sc == 0.0f || !(fabsf(sc) <= 3.402823466e38f)) sc = (mn != 0.0f) ? fabsf(mn) : 1.0f;
     const float zp = rintf(-mn / sc);
+    const Quot qt(sc);
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float q = rintf(x[i] / sc) + zp;
+      float q = rintf(qt(x[i])) + zp;
       q = fminf(fmaxf(q, 0.0f), 15.0f);
       packed |= ((uint32_t)q) << (4 * i);
     }
@@ -59,14 +60,23 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
     if (j == 0) *reinterpret_cast<float2*>(meta_row) = make_float2(sc, zp);
     return;
   }
-  uint32_t lo = 0, hi = 0;
+  const Quot qt(s);
+  float t[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t c;
-    if (dtype == DT_INT8) c = enc_int8(x[i], s);
-    else if (dtype == DT_E4M3) c = enc_fp8<DT_E4M3>(x[i], s);
-    else c = enc_fp8<DT_E5M2>(x[i], s);
-    if (i < 4) lo |= c << (8 * i); else hi |= c << (8 * (i - 4));
+  for (int i = 0; i < 8; ++i) t[i / 4][i % 4] = qt(x[i]);
+  uint32_t lo = 0, hi = 0;
+  if (dtype == DT_INT8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= enc_int8(t[0][i]) << (8 * i);
+      hi |= enc_int8(t[1][i]) << (8 * i);
+    }
+  } else if (dtype == DT_E4M3) {
+    lo = enc_fp8x4<DT_E4M3>(t[0]);
+    hi = enc_fp8x4<DT_E4M3>(t[1]);
+  } else {
+    lo = enc_fp8x4<DT_E5M2>(t[0]);
+    hi = enc_fp8x4<DT_E5M2>(t[1]);
   }
   *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
 }

@@ -47,50 +47,73 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // encoders
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t enc_int8(float x, float s) {
-  float t = x / s;
+// x / s as the correctly rounded float32 quotient, from r = 1 / s (one division
+// per scale instead of one per element): q0 = x r is within an ulp of x / s, the
+// residual x - q0 s is exact through fma, and one correction step q0 + r (x - q0 s)
+// rounds to the correctly rounded quotient (Markstein's theorem, given r
+// correctly rounded and no underflow or overflow in the steps).  Scales outside
+// [2^-60, 2^60] divide.  Where |q0| lies outside [2^-60, 2^60] the uncorrected
+// q0 is kept: there every encoder below gives the same code for q0 as for x / s
+// (0, or a saturated code), and inside it, with such scales, no step underflows
+// for any quotient whose code can differ from 0.
+struct Quot {
+  float s, r;
+  bool fast;
+  __device__ __forceinline__ explicit Quot(float scale) : s(scale) {
+    const float a = fabsf(scale);
+    fast = a >= 0x1p-60f && a <= 0x1p60f;
+    r = 1.0f / scale;
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    if (!fast) return x / s;
+    const float q0 = x * r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+    const float a = fabsf(q0);
+    return (a >= 0x1p-60f && a <= 0x1p60f) ? q1 : q0;
+  }
+};
+
+// INT8 code of a quotient t: RNE, clamped to [-127, 127]; NaN -> 0
+__device__ __forceinline__ uint32_t enc_int8(float t) {
   if (t != t) return 0u;
   t = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
   return (uint32_t)(int32_t)t & 0xffu;
 }
 
 template <int DT> struct Fp8Fmt;
-template <> struct Fp8Fmt<DT_E4M3> { static constexpr float kMax = 448.0f; static constexpr uint32_t kMaxCode = 0x7e; };
-template <> struct Fp8Fmt<DT_E5M2> { static constexpr float kMax = 57344.0f; static constexpr uint32_t kMaxCode = 0x7b; };
+template <> struct Fp8Fmt<DT_E4M3> { static constexpr float kMax = 448.0f; };
+template <> struct Fp8Fmt<DT_E5M2> { static constexpr float kMax = 57344.0f; };
 
-// Nearest OCP fp8 code of a float32 t, ties to even, saturating (NaN -> 0x7f|sign).
-// Implemented on the float32 bit pattern: normal results drop the low mantissa
-// bits with round-to-nearest-even (a carry moves into the exponent), subnormal
-// results are RNE of t scaled by a power of two.
+// OCP fp8 codes of four float32 values (byte i from t[i]): nearest code, ties
+// to even, saturating at the largest finite code (infinities included), and a
+// NaN becomes 0x7f with its sign.  The hardware conversion rounds to nearest
+// even; clamping its input to +-max first makes it saturate, and NaN inputs are
+// patched.  Equal to that definition on every float32 input, both formats.
 template <int DT>
-__device__ __forceinline__ uint32_t enc_fp8_value(float t) {
-  constexpr int MB = (DT == DT_E4M3) ? 3 : 2;
-  constexpr int BIAS = (DT == DT_E4M3) ? 7 : 15;
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  if ((u & 0x7fffffffu) > 0x7f800000u) return sign | 0x7fu;            // NaN
-  const float a = fabsf(t);
-  if (a >= Fp8Fmt<DT>::kMax) return sign | Fp8Fmt<DT>::kMaxCode;       // saturate (incl. Inf)
-  const float min_normal = __uint_as_float((uint32_t)(127 + 1 - BIAS) << 23);
-  uint32_t mag;
-  if (a < min_normal) {
-    // subnormal fp8: value = n * 2^(1 - BIAS - MB); n = RNE(a / 2^(1 - BIAS - MB))
-    const float inv_q = __uint_as_float((uint32_t)(127 - (1 - BIAS - MB)) << 23);
-    mag = (uint32_t)rintf(a * inv_q);                                  // exact scaling
+__device__ __forceinline__ uint32_t enc_fp8x4(const float (&t)[4]) {
+  constexpr float M = Fp8Fmt<DT>::kMax;
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(t[i], -M), M);
+  uint32_t w;
+  if constexpr (DT == DT_E4M3) {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)w, true);
   } else {
-    const uint32_t ua = __float_as_uint(a);
-    constexpr int SH = 23 - MB;
-    const uint32_t rem = ua & ((1u << SH) - 1u);
-    const uint32_t half = 1u << (SH - 1);
-    uint32_t qv = ua >> SH;
-    if (rem > half || (rem == half && (qv & 1u))) qv += 1u;
-    mag = qv - ((uint32_t)(127 - BIAS) << MB);                          // re-bias exponent
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)w, true);
   }
-  return sign | mag;
+  if ((t[0] != t[0]) | (t[1] != t[1]) | (t[2] != t[2]) | (t[3] != t[3])) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (t[i] != t[i]) {
+        const uint32_t code = ((__float_as_uint(t[i]) >> 24) & 0x80u) | 0x7fu;
+        w = (w & ~(0xffu << (8 * i))) | (code << (8 * i));
+      }
+    }
+  }
+  return w;
 }
-
-template <int DT>
-__device__ __forceinline__ uint32_t enc_fp8(float x, float s) { return enc_fp8_value<DT>(x / s); }
 
 // ---------------------------------------------------------------------------
 // byte permutes and fp16 magic-number conversions (exact)
