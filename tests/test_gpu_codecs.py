@@ -33,7 +33,9 @@ def _write_rows(dtype, rows_bits, scale, gran="per_tensor", H=1):
 
 
 @pytest.mark.parametrize("dtype", ["int8", "e4m3", "e5m2"])
-@pytest.mark.parametrize("scale", [1.0, 0.0123, 3.75e-3, 17.5, 2.0 ** -20])
+# the last three take the scale-range edges of the reciprocal-quotient path: a
+# scale outside [2^-60, 2^60] divides, one just inside does not
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 3.75e-3, 17.5, 2.0 ** -20, 2.0 ** -65, 1.5 * 2.0 ** 61, 1.01 * 2.0 ** -60])
 def test_encode_every_bf16_value(dtype, scale):
     log(f"encode all bf16: {dtype} scale={scale}")
     rows = ALL_BF16.reshape(512, 1, 128)
