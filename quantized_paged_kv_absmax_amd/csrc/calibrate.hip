@@ -28,13 +28,24 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const uint16_t* x, int
   const int64_t t0 = (int64_t)blockIdx.x * kTokensPerBlock;
   const int64_t t1 = min(T, t0 + kTokensPerBlock);
   float m = 0.0f;
-  for (int64_t t = t0 + threadIdx.x / LPR; t < t1; t += RPI) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + (t * Hkv + h) * D + 8 * j);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  // kUnroll rows per lane in flight at once; rows past t1 re-read row t1 - 1,
+  // which leaves the maximum unchanged
+  constexpr int kUnroll = 8;
+  for (int64_t t = t0 + threadIdx.x / LPR; t < t1; t += kUnroll * RPI) {
+    uint4 raw[kUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t tu = min(t + (int64_t)u * RPI, t1 - 1);
+      raw[u] = *reinterpret_cast<const uint4*>(x + (tu * Hkv + h) * D + 8 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+      }
     }
   }
 #pragma unroll
