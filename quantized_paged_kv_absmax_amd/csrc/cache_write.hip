@@ -9,6 +9,8 @@
 // (scale, zero point) pair.  Blocks in y = 0 encode K, y = 1 encode V, so a
 // launch streams both tensors; the element format is a per-launch switch that
 // is uniform across the grid.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -40,10 +42,26 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, m, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    static_assert(LPR == 8 || LPR == 16, "lanes per row");
+    // over the LPR lanes of the row (8 or 16, aligned): within quads, then
+    // half-rows (lane i with 7 - i), then rows (i with 15 - i), by DPP moves
+    // rather than LDS permutes
+    auto dpp = [](float v, auto ctrl) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using Xor1 = std::integral_constant<int, 0xB1>;   // quad_perm [1, 0, 3, 2]
+    using Xor2 = std::integral_constant<int, 0x4E>;   // quad_perm [2, 3, 0, 1]
+    using HalfMirror = std::integral_constant<int, 0x141>;
+    using Mirror = std::integral_constant<int, 0x140>;
+    mn = fminf(mn, dpp(mn, Xor1{}));
+    mx = fmaxf(mx, dpp(mx, Xor1{}));
+    mn = fminf(mn, dpp(mn, Xor2{}));
+    mx = fmaxf(mx, dpp(mx, Xor2{}));
+    mn = fminf(mn, dpp(mn, HalfMirror{}));
+    mx = fmaxf(mx, dpp(mx, HalfMirror{}));
+    if constexpr (LPR == 16) {
+      mn = fminf(mn, dpp(mn, Mirror{}));
+      mx = fmaxf(mx, dpp(mx, Mirror{}));
     }
     float sc = (mx - mn) / 15.0f;
     if (sc == 0.0f || !(fabsf(sc) <= 3.402823466e38f)) sc = (mn != 0.0f) ? fabsf(mn) : 1.0f;
