@@ -366,7 +366,7 @@ def cpu_baseline(min_s=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
+        print(json.dumps({"error": "this benchmark measures one GPU only: the decode path runs on a single MI355X; "
                                    "run with --gpus 1"}))
         sys.exit(2)
     if args.copy_probe:
