@@ -352,16 +352,16 @@ __device__ __forceinline__ float unpack_hi(uint32_t v, bool bf) {
 }
 
 // fp16 pair of the remainders (a - h.lo, b - h.hi), h the fp16 pair of (a, b):
-// each remainder is exact in fp32 (h is a rounded to 11 bits), so one mixed
-// fma per element, reading its half of h as fp16, gives the same bits as
-// converting h back, subtracting and packing
-__device__ __forceinline__ uint32_t f16_remainders(float a, float b, uint32_t h) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
-      "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "=&v"(r)
-      : "v"(h), "v"(a), "v"(b));
-  return r;
+// each remainder is exact in fp32 (h is a rounded to 11 bits), so a mixed fma
+// per element, h's half read as fp16 times m1 = -1 plus the element, gives the
+// same bits as converting h back and subtracting.  m1 is -1 hidden from the
+// optimiser (which would fold it into a subtraction of a reconverted h), and h
+// must come in opaque for the same reason; the instructions stay the
+// compiler's own, so it keeps their hazards with the MFMAs that read the result.
+__device__ __forceinline__ uint32_t f16_remainders(float a, float b, uint32_t h, float m1) {
+  const f16x2 hv = __builtin_bit_cast(f16x2, h);
+  const f16x2 v = {(_Float16)__builtin_fmaf((float)hv[0], m1, a), (_Float16)__builtin_fmaf((float)hv[1], m1, b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1075,6 +1075,9 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     }
   };
 
+  float m1 = -1.0f;                 // -1, opaque to the optimiser (f16_remainders)
+  asm("" : "+v"(m1));
+
   // ---- segment state ----
   // query operand: head c (zero if c >= g), in the k order of the K operand.
   // Integer path: q = sq * (q2 + q1 / 128 + q0 / 16384), three int8 digits and a
@@ -1365,22 +1368,15 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     }
     const float msub = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
-    // PV, two pages per MFMA (32 tokens)
+    // PV, two pages per MFMA (32 tokens): the V operands of the page pair, then
+    // the weights and the products
 #pragma unroll
     for (int i = 0; i < CH; i += 2) {
-      u32x4 aop;
-      u32x4 aop_lo;   // weights w = w_hi + w_lo (w_hi alone carries 8 or 11 bits)
       u32x2 vop[2][NE];
+      float vs[2][4], vz[2][4];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int pi = i + h2;
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(sl[pi][r] - msub);     // -inf -> 0
-          if constexpr (VT == DT_INT4) l_run += pr[r];
-        }
-        uint32_t a0, a1;
         // V rows 4qg..4qg+3 of the page, this lane's columns (and INT4 metadata)
         uint32_t vw[4][VG::kVDw];
 #pragma unroll
@@ -1393,39 +1389,12 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
             vw[r][0] = vraw4[pi][r];
           }
         }
-        const u32x4 vm0r = vm[pi][0], vm1r = vm[pi][1];
         if constexpr (VT == DT_INT4) {
-          const float4 vm0 = __builtin_bit_cast(float4, vm0r);
-          const float4 vm1 = __builtin_bit_cast(float4, vm1r);
-          const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
-          const float vz[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
-          // only the sequence's last page holds unwritten slots, whose metadata
-          // may be NaN: there a zero weight must not meet it
-          float ps[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ps[r] = (!TAIL || pr[r] != 0.0f) ? pr[r] * vs[r] : 0.0f;
-          a0 = pack2(ps[0], ps[1], true);
-          a1 = pack2(ps[2], ps[3], true);
-          aop_lo[2 * h2] = pack2(ps[0] - unpack_lo(a0, true), ps[1] - unpack_hi(a0, true), true);
-          aop_lo[2 * h2 + 1] = pack2(ps[2] - unpack_lo(a1, true), ps[3] - unpack_hi(a1, true), true);
-          // the zero-point term from the unrounded weights (hi + lo equals them to
-          // about 2^-17; this keeps the error off the term zp, which is unbounded)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) corr_run += (!TAIL || ps[r] != 0.0f) ? ps[r] * vz[r] : 0.0f;
-        } else {
-          a0 = pack2(pr[0], pr[1], VBF);
-          a1 = pack2(pr[2], pr[3], VBF);
+          const float4 vm0 = __builtin_bit_cast(float4, vm[pi][0]);
+          const float4 vm1 = __builtin_bit_cast(float4, vm[pi][1]);
+          vs[h2][0] = vm0.x; vs[h2][1] = vm0.z; vs[h2][2] = vm1.x; vs[h2][3] = vm1.z;
+          vz[h2][0] = vm0.y; vz[h2][1] = vm0.w; vz[h2][2] = vm1.y; vz[h2][3] = vm1.w;
         }
-        aop[2 * h2] = a0;
-        aop[2 * h2 + 1] = a1;
-        if constexpr (VT != DT_INT4 && WBF) {
-          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
-          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
-        } else if constexpr (VT != DT_INT4 && WSPLIT) {
-          aop_lo[2 * h2] = f16_remainders(pr[0], pr[1], a0);
-          aop_lo[2 * h2 + 1] = f16_remainders(pr[2], pr[3], a1);
-        }
-
         v_operands<VT, D>(vw, vop[h2]);
         if constexpr (TAIL && V_NAN) {
           // tokens past the end of the sequence: their slots may hold NaN codes
@@ -1437,6 +1406,47 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
             vop[h2][e][0] &= m01;
             vop[h2][e][1] &= m23;
           }
+        }
+      }
+      u32x4 aop;
+      u32x4 aop_lo;   // weights w = w_hi + w_lo (w_hi alone carries 8 or 11 bits)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pi = i + h2;
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(sl[pi][r] - msub);     // -inf -> 0
+          if constexpr (VT == DT_INT4) l_run += pr[r];
+        }
+        uint32_t a0, a1;
+        if constexpr (VT == DT_INT4) {
+          // only the sequence's last page holds unwritten slots, whose metadata
+          // may be NaN: there a zero weight must not meet it
+          float ps[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ps[r] = (!TAIL || pr[r] != 0.0f) ? pr[r] * vs[h2][r] : 0.0f;
+          a0 = pack2(ps[0], ps[1], true);
+          a1 = pack2(ps[2], ps[3], true);
+          aop_lo[2 * h2] = pack2(ps[0] - unpack_lo(a0, true), ps[1] - unpack_hi(a0, true), true);
+          aop_lo[2 * h2 + 1] = pack2(ps[2] - unpack_lo(a1, true), ps[3] - unpack_hi(a1, true), true);
+          // the zero-point term from the unrounded weights (hi + lo equals them to
+          // about 2^-17; this keeps the error off the term zp, which is unbounded)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) corr_run += (!TAIL || ps[r] != 0.0f) ? ps[r] * vz[h2][r] : 0.0f;
+        } else {
+          a0 = pack2(pr[0], pr[1], VBF);
+          a1 = pack2(pr[2], pr[3], VBF);
+        }
+        aop[2 * h2] = a0;
+        aop[2 * h2 + 1] = a1;
+        if constexpr (VT != DT_INT4 && WBF) {
+          aop_lo[2 * h2] = pack2(pr[0] - unpack_lo(a0, true), pr[1] - unpack_hi(a0, true), true);
+          aop_lo[2 * h2 + 1] = pack2(pr[2] - unpack_lo(a1, true), pr[3] - unpack_hi(a1, true), true);
+        } else if constexpr (VT != DT_INT4 && WSPLIT) {
+          asm("" : "+v"(a0), "+v"(a1));
+          aop_lo[2 * h2] = f16_remainders(pr[0], pr[1], a0, m1);
+          aop_lo[2 * h2 + 1] = f16_remainders(pr[2], pr[3], a1, m1);
         }
       }
 #pragma unroll
