@@ -134,34 +134,20 @@ __device__ __forceinline__ int clamp_len(const Params& p, int b, bool count) {
 template <int DT, int D, int N>
 __device__ __forceinline__ u32x4 k_operand(const uint32_t (&kw)[N], int s) {
   static_assert(N == Geo<DT, D>::kKDw, "K lane width");
+  static_assert(DT == DT_BF16 || DT == DT_E4M3 || DT == DT_E5M2, "INT8 / INT4 K take the integer path");
   u32x4 o;
   if constexpr (DT == DT_BF16) {
     o[0] = kw[4 * s]; o[1] = kw[4 * s + 1]; o[2] = kw[4 * s + 2]; o[3] = kw[4 * s + 3];
-  } else if constexpr (DT == DT_INT8) {
-    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    const uint32_t a = kw[2 * s] ^ 0x80808080u, b = kw[2 * s + 1] ^ 0x80808080u;
-    o[0] = pk_add_f16(perm(kMagic64, a, kSelLo), bias);
-    o[1] = pk_add_f16(perm(kMagic64, a, kSelHi), bias);
-    o[2] = pk_add_f16(perm(kMagic64, b, kSelLo), bias);
-    o[3] = pk_add_f16(perm(kMagic64, b, kSelHi), bias);
   } else if constexpr (DT == DT_E4M3) {
     o[0] = e4m3x2_to_f16x2<false>(kw[2 * s]);
     o[1] = e4m3x2_to_f16x2<true>(kw[2 * s]);
     o[2] = e4m3x2_to_f16x2<false>(kw[2 * s + 1]);
     o[3] = e4m3x2_to_f16x2<true>(kw[2 * s + 1]);
-  } else if constexpr (DT == DT_E5M2) {
+  } else {  // E5M2: the code byte is the fp16 high byte
     o[0] = perm(0u, kw[2 * s], 0x010C000Cu);
     o[1] = perm(0u, kw[2 * s], 0x030C020Cu);
     o[2] = perm(0u, kw[2 * s + 1], 0x010C000Cu);
     o[3] = perm(0u, kw[2 * s + 1], 0x030C020Cu);
-  } else {  // INT4: element order (even d of bytes 0..3, then odd d of bytes 0..3)
-    const f16x2 bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    const uint32_t w = kw[s];
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    o[0] = pk_add_f16(perm(kMagic64, lo, kSelLo), bias);
-    o[1] = pk_add_f16(perm(kMagic64, lo, kSelHi), bias);
-    o[2] = pk_add_f16(perm(kMagic64, hi, kSelLo), bias);
-    o[3] = pk_add_f16(perm(kMagic64, hi, kSelHi), bias);
   }
   return o;
 }
@@ -375,34 +361,6 @@ constexpr int kRsrcFlags = 0x00020000;   // gfx9 buffer descriptor word 3 (raw 3
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
-}
-
-template <int NDW>
-__device__ __forceinline__ void buf_load(uint32_t (&r)[NDW], __amdgpu_buffer_rsrc_t rs, int off) {
-  if constexpr (NDW % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < NDW / 4; ++i) {
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0));
-      r[4 * i] = v[0]; r[4 * i + 1] = v[1]; r[4 * i + 2] = v[2]; r[4 * i + 3] = v[3];
-    }
-  } else if constexpr (NDW == 2) {
-    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
-    r[0] = v[0]; r[1] = v[1];
-  } else {
-    static_assert(NDW == 1, "unsupported load width");
-    r[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-  }
-}
-
-// V bytes of one row for this lane: VRB bytes (2, 4, 8 or 16)
-template <int DT, int D, int N>
-__device__ __forceinline__ void buf_load_v_row(uint32_t (&r)[N], __amdgpu_buffer_rsrc_t rs, int off) {
-  static_assert(N == Geo<DT, D>::kVDw, "V row width");
-  if constexpr (Geo<DT, D>::kVRowBytes == 2) {
-    r[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
-  } else {
-    buf_load<N>(r, rs, off);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -649,17 +607,6 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
   } else {
     wait_vmcnt<0>();
   }
-}
-
-template <int LPR, int NST>
-__device__ __forceinline__ void wait_rounds_after(int rounds_after) {
-  // rounds_after in [0, NST-1]: the loads of that many later rounds may stay in flight
-  static_assert(NST <= 5, "wait table");
-  if (rounds_after <= 0) wait_vmcnt<0>();
-  else if (rounds_after == 1) wait_vmcnt<(1 * LPR < 63 ? 1 * LPR : 63)>();
-  else if (rounds_after == 2) wait_vmcnt<(2 * LPR < 63 ? 2 * LPR : 63)>();
-  else if (rounds_after == 3) wait_vmcnt<(3 * LPR < 63 ? 3 * LPR : 63)>();
-  else wait_vmcnt<(4 * LPR < 63 ? 4 * LPR : 63)>();
 }
 
 // lazy rescaling: the exponent reference of a head moves only when a logit exceeds

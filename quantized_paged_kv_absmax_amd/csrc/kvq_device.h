@@ -131,11 +131,6 @@ constexpr uint32_t kMagic43 = 0x43434343u;
 constexpr uint32_t kSelLo = 0x04010400u;
 constexpr uint32_t kSelHi = 0x04030402u;
 
-__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, f16x2 b) {
-  f16x2 v = __builtin_bit_cast(f16x2, a) + b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 // fp8 e4m3 pair (bytes 0,1 or 2,3 of w) -> two fp16 (exact; NaN stays NaN)
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
@@ -147,7 +142,6 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
 // wave helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // max / sum of v over the lane pairs (l, l ^ 16), or (l, l ^ 32), through the
 // gfx950 row-swap instructions instead of the LDS crossbar.  Swapping v with
