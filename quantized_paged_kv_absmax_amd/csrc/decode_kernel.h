@@ -660,8 +660,9 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // (token, head) row arithmetic folds away.  With MQ a workgroup of up to four
 // waves, one per 16-column tile, shares each round: every wave DMAs a share of
 // the round's pages into the common LDS stage, waits for its share, and a
-// barrier makes the whole round visible; a second barrier after the round's
-// arithmetic frees the stage for the next DMA.  The page bytes are then read
+// barrier makes the whole round visible; a second barrier, once every wave has
+// read the round into registers, frees the stage, and the round after next is
+// issued into it before the round's arithmetic.  The page bytes are then read
 // once for all the tiles of a workgroup.
 template <int KT, int VT, int D, int CH, bool MQ>
 __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
