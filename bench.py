@@ -144,9 +144,15 @@ def kv_bytes(inp):
 
 
 def decode_source_hash():
+    """Hash of the decode kernels' source with comments and blank space removed, so
+    that a profile stays matched to its kernel across edits of comments only."""
+    import re
     h = hashlib.sha256()
     for f in ("decode_kernel.h", "decode.hip", "kvq_device.h"):
-        h.update(open(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
