@@ -46,6 +46,9 @@ def parse():
                     help="only run 5 device-to-device copies of BYTES bytes (calibrates HBM byte counters)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
                     help="write the text summary of a rocprofv3 --kernel-trace --stats csv run and exit")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("CSV_A", "CSV_B", "OUT", "COMMAND"),
+                    help="write per-page instruction and wait counters of the chunk kernels (headline decode "
+                         "and 16-token verify) from two rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=7,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES", "OUT",
                              "COMMAND"),
@@ -66,6 +69,47 @@ def trace_summary(stats_csv, out, command):
         name = name.split("(")[0] if "kvq::" in r["Name"] else name[:64]
         lines.append(f"{name[:64]:<64} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
                      f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.1f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counter_summary(csv_a, csv_b, out, command):
+    """SQ counters of decode_chunk_kernel per 16-token page and KV head (the sum over
+    the waves that read it), averaged over dispatches: the one-token kernel on the
+    llama8b_int8 cache and the several-token kernel on verify16_int8's."""
+    import csv
+    import re
+    from workloads import WORKLOADS, make_decode_inputs
+    kernels = {"false>": "llama8b_int8", "true>": "verify16_int8"}
+    pages = {}
+    for wl in kernels.values():
+        w = WORKLOADS[wl]
+        inp = make_decode_inputs(w)
+        pages[wl] = int(((inp.seq_lens.astype(np.int64) + 15) // 16).sum()) * w.Hkv
+    per = {}   # workload -> counter -> per-page value
+    for path in (csv_a, csv_b):
+        tot, disp = {}, {}
+        for r in csv.DictReader(open(path)):
+            m = re.search(r"decode_chunk_kernel<[^>]*, (true|false)>", r["Kernel_Name"])
+            if m is None:
+                continue
+            wl = kernels[m.group(1) + ">"]
+            c = r["Counter_Name"].replace("SQ_", "")
+            tot.setdefault(wl, {})
+            tot[wl][c] = tot[wl].get(c, 0.0) + float(r["Counter_Value"])
+            disp.setdefault(wl, set()).add(r["Dispatch_Id"])
+        for wl, vals in tot.items():
+            for c, v in vals.items():
+                per.setdefault(wl, {})[c] = v / len(disp[wl]) / pages[wl]
+    lines = ["rocprofv3 SQ counters of decode_chunk_kernel per 16-token page and KV head", "", "command:",
+             "  " + command, "", "kvq_paged_attention_decode source hash: " + decode_source_hash(), "",
+             "Summed over the waves that read a page (the several-token kernel runs four, one per",
+             "16-column tile); *_CYCLES, ACTIVE_* and WAIT_* in the counters' own units.", ""]
+    for wl in kernels.values():
+        lines.append(f"{wl}: {pages[wl]} page-heads per call")
+        for c, v in sorted(per.get(wl, {}).items()):
+            lines.append(f"  {c:<28} {v:10.1f}")
+        lines.append("")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -383,6 +427,9 @@ def main():
         return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
         return
     import torch
     import quantized_paged_kv_absmax_amd as kvq
