@@ -35,11 +35,37 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, dtype, name):
+def _need(t, dtype, name, shape=None, device=None, min_numel=None):
+    """The C ABI takes bare device pointers and cannot see sizes: every tensor is
+    checked here (type, GPU residence, layout, shape) before its pointer is passed,
+    so a mismatch raises instead of reaching a kernel as an out-of-bounds access."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+
+
+def _opt(t, dtype, name, device, min_numel=1):
+    if t is not None:
+        _need(t, dtype, name, device=device, min_numel=min_numel)
+
+
+def _out_torch_dtype(odt):
+    if odt == _lib.F32:
+        return torch.float32
+    if odt == _lib.BF16:
+        return torch.bfloat16
+    raise ValueError(f"out_dtype must be bf16 or f32, got {odt}")
 
 
 def row_bytes(dtype, head_dim):
@@ -80,6 +106,8 @@ class PagedKVCache:
         of the same shape, e.g. a rotating copy)."""
         kp = self.k_pages if k_pages is None else k_pages
         vp = self.v_pages if v_pages is None else v_pages
+        _need(kp, torch.uint8, "k_pages", shape=self.k_pages.shape, device=self.k_pages.device)
+        _need(vp, torch.uint8, "v_pages", shape=self.v_pages.shape, device=self.k_pages.device)
         s = _lib.KvqCacheStruct()
         s.k_dtype, s.v_dtype, s.k_gran, s.v_gran = self.k_dtype, self.v_dtype, self.k_gran, self.v_gran
         s.num_blocks, s.block_size = self.num_blocks, self.block_size
@@ -95,7 +123,12 @@ class PagedKVCache:
 def kvq_calibrate_scales(x, granularity, target_dtype, absmax_inout, scale_out, stream=None):
     """absmax calibration of bf16 x [T][Hkv][D] into absmax_inout / scale_out (float32)."""
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 3:
+        raise ValueError(f"x must be [T][Hkv][D], got shape {tuple(x.shape)}")
     T, H, D = x.shape
+    groups = H if _gr(granularity) == _lib.PER_KV_HEAD else 1
+    _need(absmax_inout, torch.float32, "absmax_inout", device=x.device, min_numel=groups)
+    _need(scale_out, torch.float32, "scale_out", device=x.device, min_numel=groups)
     st = _lib.load().kvq_calibrate_scales(_ptr(x), T, H, D, _gr(granularity), _dt(target_dtype),
                                           _ptr(absmax_inout), _ptr(scale_out), _stream(stream))
     check(st, "kvq_calibrate_scales")
@@ -103,9 +136,13 @@ def kvq_calibrate_scales(x, granularity, target_dtype, absmax_inout, scale_out, 
 
 def kvq_cache_write(cache, k_new, v_new, slot_mapping, err_count=None, stream=None, struct=None):
     """Encode bf16 rows k_new / v_new [T][Hkv][D] into the pages at slot_mapping (int64 [T])."""
-    _need(k_new, torch.bfloat16, "k_new")
-    _need(v_new, torch.bfloat16, "v_new")
-    _need(slot_mapping, torch.int64, "slot_mapping")
+    dev = cache.k_pages.device
+    _need(k_new, torch.bfloat16, "k_new", device=dev)
+    T = k_new.shape[0] if k_new.dim() == 3 else -1
+    _need(k_new, torch.bfloat16, "k_new", shape=(T, cache.num_kv_heads, cache.head_dim))
+    _need(v_new, torch.bfloat16, "v_new", shape=(T, cache.num_kv_heads, cache.head_dim), device=dev)
+    _need(slot_mapping, torch.int64, "slot_mapping", shape=(T,), device=dev)
+    _opt(err_count, torch.int32, "err_count", dev)
     s = cache.struct() if struct is None else struct
     st = _lib.load().kvq_cache_write(ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                                      k_new.shape[0], _ptr(err_count), _stream(stream))
@@ -114,8 +151,10 @@ def kvq_cache_write(cache, k_new, v_new, slot_mapping, err_count=None, stream=No
 
 def kvq_convert_cache(cache, k_src, v_src, first_block=0, num_blocks=None, stream=None):
     """Convert bf16 pages [num_blocks][Hkv][16][D] into the cache's format."""
-    _need(k_src, torch.bfloat16, "k_src")
-    _need(v_src, torch.bfloat16, "v_src")
+    dev = cache.k_pages.device
+    shp = (cache.num_blocks, cache.num_kv_heads, cache.block_size, cache.head_dim)
+    _need(k_src, torch.bfloat16, "k_src", shape=shp, device=dev)
+    _need(v_src, torch.bfloat16, "v_src", shape=shp, device=dev)
     n = cache.num_blocks - first_block if num_blocks is None else num_blocks
     s = cache.struct()
     st = _lib.load().kvq_convert_cache(ctypes.byref(s), _ptr(k_src), _ptr(v_src), first_block, n, _stream(stream))
@@ -136,19 +175,29 @@ def kvq_paged_attention_verify(cache, q, n_q, block_tables, seq_lens, max_seq_le
     attends to cache positions up to its own.  Arguments otherwise as
     kvq_paged_attention_decode.
     """
-    _need(q, torch.bfloat16, "q")
-    _need(block_tables, torch.int32, "block_tables")
-    _need(seq_lens, torch.int32, "seq_lens")
-    T, Hq, D = q.shape
+    dev = cache.k_pages.device
+    _need(seq_lens, torch.int32, "seq_lens", device=dev)
+    if seq_lens.dim() != 1:
+        raise ValueError(f"seq_lens must be [B], got shape {tuple(seq_lens.shape)}")
     B = seq_lens.shape[0]
-    if T != B * n_q:
-        raise ValueError(f"q has {T} rows, expected batch * n_q = {B * n_q}")
+    _need(block_tables, torch.int32, "block_tables", device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_blocks], got shape {tuple(block_tables.shape)}")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B * n_q][Hq][D], got shape {tuple(q.shape)}")
+    Hq = q.shape[1]
+    _need(q, torch.bfloat16, "q", shape=(B * n_q, Hq, cache.head_dim), device=dev)
+    T, D = B * n_q, cache.head_dim
     odt = _dt(out_dtype)
     if out is None:
-        out = torch.empty((T, Hq, D), dtype=torch.float32 if odt == _lib.F32 else torch.bfloat16, device=q.device)
+        out = torch.empty((T, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+    _need(out, _out_torch_dtype(odt), "out", shape=(T, Hq, D), device=dev)
+    _opt(err_count, torch.int32, "err_count", dev)
     need = kvq_verify_workspace_size(B, n_q, Hq, cache.num_kv_heads, D, max_seq_len, partition)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
     st = _lib.load().kvq_paged_attention_verify(
@@ -183,16 +232,28 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
     block_tables int32 [B][max_blocks]; seq_lens int32 [B]; max_seq_len: host int.
     A workspace is allocated here with torch when the call needs one and none is given.
     """
-    _need(q, torch.bfloat16, "q")
-    _need(block_tables, torch.int32, "block_tables")
-    _need(seq_lens, torch.int32, "seq_lens")
-    B, Hq, D = q.shape
+    dev = cache.k_pages.device
+    _need(seq_lens, torch.int32, "seq_lens", device=dev)
+    if seq_lens.dim() != 1:
+        raise ValueError(f"seq_lens must be [B], got shape {tuple(seq_lens.shape)}")
+    B = seq_lens.shape[0]
+    _need(block_tables, torch.int32, "block_tables", device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_blocks], got shape {tuple(block_tables.shape)}")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][D], got shape {tuple(q.shape)}")
+    Hq, D = q.shape[1], cache.head_dim
+    _need(q, torch.bfloat16, "q", shape=(B, Hq, D), device=dev)
     odt = _dt(out_dtype)
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32 if odt == _lib.F32 else torch.bfloat16, device=q.device)
+        out = torch.empty((B, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+    _need(out, _out_torch_dtype(odt), "out", shape=(B, Hq, D), device=dev)
+    _opt(err_count, torch.int32, "err_count", dev)
     need = kvq_decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_seq_len, partition)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
     st = _lib.load().kvq_paged_attention_decode(

@@ -186,3 +186,25 @@ def test_capacity_accounting():
     assert kvq.kvq_cache_block_bytes(9, 1, 8, 128) == 0
     assert kvq.kvq_cache_block_bytes("int8", "int8", 0, 128) == 0
     assert kvq.kvq_blocks_in_budget(budget, "int8", "int8", 8, 128, 0) == -1
+
+
+def test_binding_rejects_host_tensors():
+    """Host tensors never reach the C ABI as device pointers: the binding raises
+    before loading the library's compute entry points."""
+    import torch
+    import quantized_paged_kv_absmax_amd as kvq
+    c = kvq.PagedKVCache(2, 2, 128, "int8", "int8", device="cpu")
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.kvq_paged_attention_decode(c, q, bt, sl, 16, 0.088)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.kvq_paged_attention_verify(c, q, 1, bt, sl, 16, 0.088)
+    x = torch.zeros((3, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.kvq_cache_write(c, x, x, torch.arange(3))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.kvq_calibrate_scales(x, "per_tensor", "int8", c.k_absmax, c.k_scale)
+    with pytest.raises(TypeError):
+        kvq.kvq_cache_write(c, x.float(), x, torch.arange(3))

@@ -208,3 +208,43 @@ def test_empty_batch_is_a_noop():
     out = kvq.kvq_paged_attention_decode(c, q, torch.zeros((0, 1), dtype=torch.int32, device="cuda"),
                                          torch.zeros(0, dtype=torch.int32, device="cuda"), 0, 0.088)
     assert out.shape == (0, 4, 128)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The C ABI sees bare pointers; the binding raises on any tensor whose shape,
+    dtype or device does not match the cache and the batch, before a launch."""
+    c = kvq.PagedKVCache(4, 2, 128, "int8", "int8")
+    dev = "cuda"
+    B, Hq = 3, 8
+    q = torch.zeros((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((B, 4), dtype=torch.int32, device=dev)
+    sl = torch.full((B,), 5, dtype=torch.int32, device=dev)
+    bad = [
+        dict(q=torch.zeros((B, Hq, 64), dtype=torch.bfloat16, device=dev)),          # head_dim of another cache
+        dict(q=torch.zeros((B - 1, Hq, 128), dtype=torch.bfloat16, device=dev)),     # fewer rows than sequences
+        dict(block_tables=torch.zeros((B - 1, 4), dtype=torch.int32, device=dev)),   # fewer tables than sequences
+        dict(block_tables=torch.zeros((B, 4), dtype=torch.int64, device=dev)),
+        dict(seq_lens=sl.cpu()),
+        dict(out=torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)),       # bf16 requested
+        dict(err_count=torch.zeros(1, dtype=torch.int64, device=dev)),
+        dict(workspace=torch.zeros(64, dtype=torch.float32, device=dev)),
+    ]
+    for over in bad:
+        args = dict(q=q, block_tables=bt, seq_lens=sl, out=None, err_count=None, workspace=None)
+        args.update(over)
+        with pytest.raises((ValueError, TypeError)):
+            kvq.kvq_paged_attention_decode(c, args["q"], args["block_tables"], args["seq_lens"], 16, 0.088,
+                                           out=args["out"], err_count=args["err_count"],
+                                           workspace=args["workspace"])
+    x = torch.zeros((5, 2, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        kvq.kvq_cache_write(c, x, x, torch.arange(4, dtype=torch.int64, device=dev))   # 4 slots for 5 rows
+    with pytest.raises(ValueError):
+        kvq.kvq_cache_write(c, x[:, :1].contiguous(), x[:, :1].contiguous(), torch.arange(5, dtype=torch.int64,
+                                                                                          device=dev))
+    with pytest.raises(ValueError):
+        kvq.kvq_convert_cache(c, torch.zeros((3, 2, 16, 128), dtype=torch.bfloat16, device=dev),
+                              torch.zeros((3, 2, 16, 128), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        kvq.kvq_calibrate_scales(x, "per_kv_head", "int8", torch.zeros(1, device=dev), torch.zeros(1, device=dev))
+    torch.cuda.synchronize()
