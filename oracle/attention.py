@@ -22,6 +22,11 @@ gives (m_j, l_j, acc_j) = (max z, sum exp(z - m_j), sum exp(z - m_j) v_hat), and
 Several query tokens per sequence (``verify``): token i of the last n_q
 positions attends causally to positions 0..L_b - n_q + i.
 
+Rotated keys (K dtype "int4h", KVarN's rotation step, techfi24's KVarN article,
+"Contexte Technique"): the cache holds INT4 codes of H k; the query is rotated
+the same way (H q, rounded to bf16 as the caller hands it over) and the logit
+scale is divided by D, since (H q) . (H k) = D (q . k).
+
 Pins (tests/test_oracle_attention.py): q = 0 gives the mean of v_hat; one
 token gives v_hat_0; adding a constant to every logit changes nothing; a
 permuted page pool gives bit-identical output to the contiguous order; g = 1
@@ -32,6 +37,15 @@ on the same decoded tensors; split == unsplit.
 import numpy as np
 
 from . import codecs
+
+
+def _rotated_query(cache, q_bits):
+    """Rotated-key caches take H q (bf16), others q itself."""
+    return codecs.hadamard_rotate_bf16(q_bits) if cache.k_dtype == "int4h" else q_bits
+
+
+def _logit_divisor(cache):
+    return cache.D if cache.k_dtype == "int4h" else 1
 
 
 def _attend(qv, K, V, softmax_scale):
@@ -50,10 +64,11 @@ def decode(cache, q_bits, block_tables, seq_lens, softmax_scale, heads=None, seq
     caller passes (used exactly).  ``heads`` / ``seqs`` restrict the work to a
     subset (other rows are left NaN), for sampled checks at large sizes.
     """
+    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     B, Hq, D = q.shape
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale))
+    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
     out = np.full((B, Hq, D), np.nan)
     for b in (range(B) if seqs is None else seqs):
         L = int(seq_lens[b])
@@ -86,11 +101,12 @@ def verify(cache, q_bits, n_q, block_tables, seq_lens, softmax_scale, heads=None
     p < 0 (a sequence shorter than n_q) gives a zero row.  ``heads`` / ``seqs``
     restrict the work (other rows NaN).
     """
+    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     T, Hq, D = q.shape
     B = T // n_q
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale))
+    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
     out = np.full((T, Hq, D), np.nan)
     for b in (range(B) if seqs is None else seqs):
         L = int(seq_lens[b])
@@ -118,10 +134,11 @@ def decode_partials(cache, q_bits, block_tables, seq_lens, softmax_scale, partit
     partitions of the longest sequence.  Partitions with no tokens hold
     m = -inf, l = 0, acc = 0.
     """
+    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     B, Hq, D = q.shape
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale))
+    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
     Lmax = max(int(x) for x in seq_lens) if len(seq_lens) else 0
     P = max(1, -(-Lmax // partition))
     m = np.full((B, Hq, P), -np.inf)

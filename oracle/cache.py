@@ -20,12 +20,13 @@ import numpy as np
 from . import codecs
 
 F32 = np.float32
-CODE_DTYPES = ("bf16", "int8", "e4m3", "e5m2", "int4")
+# int4h: INT4 asymmetric of the Hadamard-rotated row (K only; codecs.hadamard_rotate_bf16)
+CODE_DTYPES = ("bf16", "int8", "e4m3", "e5m2", "int4", "int4h")
 QMAX = {"int8": 127.0, "e4m3": 448.0, "e5m2": 57344.0}
 
 
 def row_bytes(dtype, D):
-    return {"bf16": 2 * D, "int8": D, "e4m3": D, "e5m2": D, "int4": D // 2}[dtype]
+    return {"bf16": 2 * D, "int8": D, "e4m3": D, "e5m2": D, "int4": D // 2, "int4h": D // 2}[dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -94,6 +95,8 @@ def encode_rows(x_bits, dtype, scale=None):
     N, H, D = x_bits.shape
     if dtype == "bf16":
         return x_bits.view(np.uint8).reshape(N, H, 2 * D).copy(), None
+    if dtype == "int4h":
+        x_bits, dtype = codecs.hadamard_rotate_bf16(x_bits), "int4"
     x = codecs.bf16_to_f32(x_bits)
     if dtype == "int4":
         codes, s, zp = codecs.int4_encode_rows(x)
@@ -113,7 +116,7 @@ def decode_rows(b, dtype, D, scale=None, meta=None):
     H = b.shape[-2]
     if dtype == "bf16":
         return codecs.bf16_to_f32(b.view(np.uint16))
-    if dtype == "int4":
+    if dtype in ("int4", "int4h"):   # int4h: the rotated row
         codes = codecs.int4_unpack(b)
         return codecs.int4_decode(codes, meta[..., 0], meta[..., 1])
     s = _head_scale(scale, H)[:, None]
@@ -139,8 +142,8 @@ class PagedCache:
         shape = (num_blocks, num_kv_heads, block_size)
         self.k_pages = np.full(shape + (row_bytes(k_dtype, head_dim),), fill, np.uint8)
         self.v_pages = np.full(shape + (row_bytes(v_dtype, head_dim),), fill, np.uint8)
-        self.k_meta = np.full(shape + (2,), np.nan, F32) if k_dtype == "int4" else None
-        self.v_meta = np.full(shape + (2,), np.nan, F32) if v_dtype == "int4" else None
+        self.k_meta = np.full(shape + (2,), np.nan, F32) if k_dtype in ("int4", "int4h") else None
+        self.v_meta = np.full(shape + (2,), np.nan, F32) if v_dtype in ("int4", "int4h") else None
 
     # -- write -------------------------------------------------------------
     def write(self, k_bits, v_bits, slot_mapping):

@@ -19,6 +19,10 @@ Pins (tests/test_oracle_codecs.py):
                       constant rows, hand-packed nibble order.
   kv_bytes_per_token_head - the 2.00x GPU-block ratios printed in the L4 table
                       of vLLM PR 4893 (FP16 vs FP8 KV at equal memory).
+  hadamard_rotate_bf16 - scipy's Sylvester Hadamard matrix in float64 (exact on
+                      integer rows, within the bf16 rounding otherwise), H H = D I,
+                      the closed-form columns (-1)^popcount(i & k), and preserved
+                      dot products.
 """
 
 import numpy as np
@@ -272,6 +276,34 @@ def int4_decode(codes, s, zp):
 # byte accounting
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Hadamard rotation of a row (the rotation step of KVarN: techfi24's KVarN
+# article, "Contexte Technique").  Reading: the unnormalised Sylvester-Hadamard
+# transform of the row's D values, H x with H[i][k] = (-1)^popcount(i & k), taken
+# in float32 by the fast Walsh-Hadamard butterfly (stages h = 1, 2, 4, ..., D/2;
+# the pair at indices (i, i + h), i & h == 0, becomes (a + b, a - b)) and rounded
+# to bf16.  H H = D I, so (H q) . (H k) = D (q . k): the logit scale takes 1 / D.
+# ---------------------------------------------------------------------------
+
+
+def hadamard_rotate_bf16(x_bits):
+    """bf16 rows [..., D] (D a power of two) -> bf16 bits of H x, as above."""
+    x = bf16_to_f32(np.asarray(x_bits, np.uint16)).astype(F32).copy()
+    D = x.shape[-1]
+    assert D & (D - 1) == 0
+    lead = x.shape[:-1]
+    h = 1
+    while h < D:
+        y = x.reshape(lead + (D // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b          # float32 arithmetic, round to nearest even
+        y[..., 1, :] = a - b
+        x = y.reshape(lead + (D,))
+        h *= 2
+    return f32_to_bf16_rne(x)
+
+
 INT4_META_BYTES = 8  # float32 scale + float32 zero point per (token, KV head)
 
 
@@ -281,7 +313,7 @@ def elem_bytes_per_row(dtype, D):
         return 2 * D
     if dtype in ("int8", "e4m3", "e5m2"):
         return D
-    if dtype == "int4":
+    if dtype in ("int4", "int4h"):
         return D // 2 + INT4_META_BYTES
     raise ValueError(dtype)
 

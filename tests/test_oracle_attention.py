@@ -187,3 +187,32 @@ def test_verify_zero_query_gives_prefix_mean():
             for h in range(inp.w.Hq):
                 np.testing.assert_allclose(out[b * n_q + i, h], V[:L - n_q + i + 1, h // g].mean(axis=0),
                                            rtol=0, atol=1e-14)
+
+
+def test_rotated_keys_equal_derotated_attention():
+    """An "int4h" cache stores INT4 codes of H k; its decode rotates q and divides
+    the logit scale by D.  De-rotating the stored keys (H^-1 = H / D) must then
+    give the same attention with the plain query: catches a missing 1 / D, an
+    unrotated or differently rotated query."""
+    from scipy.linalg import hadamard
+    inp = _inputs(B=2, lens=("fixed", (9, 40)), Hq=4, Hkv=2, D=64)
+    c = oc.PagedCache(inp.num_blocks, 2, 64, "int4h", "int4")
+    c.write(inp.k_bits, inp.v_bits, inp.slot_mapping)
+    rng = np.random.default_rng(14)
+    q = rng.integers(-2, 3, size=inp.q_bits.shape).astype(np.float32)   # rotation exact in bf16
+    q_bits = codecs.f32_to_bf16_rne(q)
+    out = oa.decode(c, q_bits, inp.block_tables, inp.seq_lens, 0.125)
+    H = hadamard(64).astype(np.float64)
+    for b in range(2):
+        L = int(inp.seq_lens[b])
+        Kr = c.gather(inp.block_tables[b], L, "k").astype(np.float64)        # H k, dequantised
+        V = c.gather(inp.block_tables[b], L, "v").astype(np.float64)
+        K = Kr @ H / 64.0                                                   # H symmetric, H H = 64 I
+        for h in range(4):
+            ref = oa._attend(q[b, h].astype(np.float64), K[:, h // 2, :], V[:, h // 2, :], 0.125)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+    # and the stored codes are those of the rotated rows
+    plain = oc.PagedCache(inp.num_blocks, 2, 64, "int4", "int4")
+    plain.write(codecs.hadamard_rotate_bf16(inp.k_bits), inp.v_bits, inp.slot_mapping)
+    assert np.array_equal(plain.k_pages, c.k_pages)
+    assert np.array_equal(plain.k_meta, c.k_meta, equal_nan=True)

@@ -248,3 +248,49 @@ def test_block_ratio_matches_l4_table():
         n8 = codecs.blocks_in_budget(budget, "e5m2", "e5m2", 128, 8, 32)
         assert n16 == base_blocks
         assert n8 / n16 == ratio == 2.0
+
+
+# ---- Hadamard rotation (KVarN's rotation step) ----
+
+def _bf16_bits(x):
+    return codecs.f32_to_bf16_rne(np.asarray(x, np.float32))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_matches_sylvester_matrix(D):
+    from scipy.linalg import hadamard
+    H = hadamard(D).astype(np.float64)
+    rng = np.random.default_rng(11)
+    xi = rng.integers(-2, 3, size=(40, D)).astype(np.float32)        # exact in bf16 and in the sums
+    got = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(xi))).astype(np.float64)
+    assert np.array_equal(got, xi.astype(np.float64) @ H.T)
+    xr = codecs.bf16_to_f32(_bf16_bits(rng.standard_normal((200, D)) * 3.0))
+    ref = xr.astype(np.float64) @ H.T
+    got = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(xr))).astype(np.float64)
+    # bf16 rounding of the result (2^-9 relative) plus float32 sums (about 2^-24 * D * max|x|)
+    bound = np.abs(ref) * 2.0 ** -8 + 2.0 ** -20 * D * np.abs(xr).max(axis=-1, keepdims=True)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_hadamard_twice_is_D_times_identity_and_columns():
+    D = 128
+    rng = np.random.default_rng(12)
+    x = rng.integers(-2, 3, size=(30, D)).astype(np.float32)
+    once = codecs.hadamard_rotate_bf16(_bf16_bits(x))
+    twice = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(once))
+    assert np.array_equal(twice, D * x)
+    eye = np.eye(D, dtype=np.float32)
+    cols = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(eye)))
+    i, k = np.meshgrid(np.arange(D), np.arange(D), indexing="ij")
+    pop = np.vectorize(lambda v: bin(v).count("1"))(i & k)
+    assert np.array_equal(cols, np.where(pop % 2 == 0, 1.0, -1.0).astype(np.float32))
+
+
+def test_hadamard_preserves_dot_products():
+    D = 64
+    rng = np.random.default_rng(13)
+    q = rng.integers(-2, 3, size=(20, D)).astype(np.float32)
+    k = rng.integers(-2, 3, size=(20, D)).astype(np.float32)
+    hq = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(q))).astype(np.float64)
+    hk = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(k))).astype(np.float64)
+    assert np.array_equal((hq * hk).sum(-1), D * (q.astype(np.float64) * k).sum(-1))
