@@ -177,7 +177,7 @@ def copy_probe(nbytes):
 # bytes one (token, KV head) row of K or V occupies: codes, plus the float32
 # (scale, zero point) pair of INT4
 ROW_BYTES = {"bf16": lambda D: 2 * D, "int8": lambda D: D, "e4m3": lambda D: D, "e5m2": lambda D: D,
-             "int4": lambda D: D // 2 + 8}
+             "int4": lambda D: D // 2 + 8, "int4h": lambda D: D // 2 + 8}
 
 
 def kv_bytes(inp):
@@ -457,7 +457,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
-        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "longctx_int8",
+        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "int4_had", "longctx_int8",
                  "verify16_int8"]
         if args.only:
             names = [n for n in args.only.split(",") if n]

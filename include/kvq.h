@@ -76,7 +76,16 @@ typedef enum kvq_dtype {
   KVQ_FP8_E4M3 = 2,
   KVQ_FP8_E5M2 = 3,
   KVQ_INT4_ASYM = 4,
-  KVQ_F32 = 5
+  KVQ_F32 = 5,
+  /* Keys only: KVQ_INT4_ASYM codes of the Hadamard-rotated row (KVarN article,
+   * technical context: a Hadamard rotation before asymmetric quantisation).  The
+   * rotation is the unnormalised Sylvester-Hadamard transform H x of the head_dim
+   * values, in float32 by the fast Walsh-Hadamard butterfly (stages h = 1, 2, ...,
+   * head_dim / 2, the pair at (i, i + h) becoming (a + b, a - b)), rounded to bf16.
+   * Decoding such a cache takes the query rotated by kvq_hadamard_rotate and
+   * softmax_scale / head_dim, since (H q) . (H k) = head_dim (q . k).  Values and
+   * metadata are laid out as KVQ_INT4_ASYM; V must be KVQ_INT4_ASYM. */
+  KVQ_INT4_HAD = 6
 } kvq_dtype;
 
 typedef enum kvq_granularity {
@@ -272,6 +281,19 @@ uint64_t kvq_cache_block_bytes(int32_t k_dtype, int32_t v_dtype, int32_t num_kv_
  */
 int64_t kvq_blocks_in_budget(uint64_t budget_bytes, int32_t k_dtype, int32_t v_dtype, int32_t num_kv_heads,
                              int32_t head_dim, int32_t num_layers, int32_t block_size);
+
+/*
+ * kvq_hadamard_rotate — the KVQ_INT4_HAD rotation of bf16 rows (KVarN article,
+ * technical context), for the query of a decode over rotated keys.
+ *   x, out      (device) bf16 [num_rows][head_dim], 16-byte aligned; out may
+ *               equal x (each row is read before it is written)
+ *   num_rows    >= 0;  head_dim 64 or 128
+ * Each output row is bf16(H x) as described at KVQ_INT4_HAD.  Errors:
+ * KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (head_dim),
+ * KVQ_ERR_HIP.
+ */
+kvq_status kvq_hadamard_rotate(const uint16_t* x, int64_t num_rows, int32_t head_dim, uint16_t* out,
+                               void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kvq_status_string(int32_t status);

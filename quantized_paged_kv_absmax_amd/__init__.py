@@ -7,11 +7,11 @@ library; the first call does, and raises ImportError if it has not been built
 """
 
 from ._lib import (  # noqa: F401
-    BF16, INT8, FP8_E4M3, FP8_E5M2, INT4_ASYM, F32, PER_TENSOR, PER_KV_HEAD, PER_TOKEN_HEAD,
+    BF16, INT8, FP8_E4M3, FP8_E5M2, INT4_ASYM, INT4_HAD, F32, PER_TENSOR, PER_KV_HEAD, PER_TOKEN_HEAD,
     KvqError, LIB_PATH, load,
 )
 from .api import (  # noqa: F401
     PagedKVCache, kvq_calibrate_scales, kvq_cache_write, kvq_convert_cache, kvq_decode_workspace_size,
     kvq_paged_attention_decode, kvq_paged_attention_verify, kvq_verify_workspace_size, kvq_cache_block_bytes,
-    kvq_blocks_in_budget, row_bytes,
+    kvq_blocks_in_budget, kvq_hadamard_rotate, row_bytes,
 )

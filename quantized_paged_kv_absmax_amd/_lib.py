@@ -12,17 +12,18 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libk
 # kvq_status
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 # kvq_dtype
-BF16, INT8, FP8_E4M3, FP8_E5M2, INT4_ASYM, F32 = range(6)
+BF16, INT8, FP8_E4M3, FP8_E5M2, INT4_ASYM, F32, INT4_HAD = range(7)
 # kvq_granularity
 PER_TENSOR, PER_KV_HEAD, PER_TOKEN_HEAD = range(3)
 
 DTYPES = {"bf16": BF16, "auto": BF16, "int8": INT8, "e4m3": FP8_E4M3, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
-          "e5m2": FP8_E5M2, "fp8_e5m2": FP8_E5M2, "int4": INT4_ASYM, "f32": F32}
+          "e5m2": FP8_E5M2, "fp8_e5m2": FP8_E5M2, "int4": INT4_ASYM, "f32": F32, "int4h": INT4_HAD}
 GRANULARITIES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD, "per_token_head": PER_TOKEN_HEAD}
 
 EXPORTS = ("kvq_calibrate_scales", "kvq_cache_write", "kvq_convert_cache", "kvq_decode_workspace_size",
            "kvq_paged_attention_decode", "kvq_paged_attention_verify", "kvq_verify_workspace_size",
-           "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string", "kvq_abi_version")
+           "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string", "kvq_abi_version",
+           "kvq_hadamard_rotate")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -68,6 +69,8 @@ def load():
     lib.kvq_cache_block_bytes.restype = ctypes.c_uint64
     lib.kvq_blocks_in_budget.argtypes = [ctypes.c_uint64, I32, I32, I32, I32, I32, I32]
     lib.kvq_blocks_in_budget.restype = ctypes.c_int64
+    lib.kvq_hadamard_rotate.argtypes = [P, I64, I32, P, P]
+    lib.kvq_hadamard_rotate.restype = I32
     lib.kvq_status_string.argtypes = [I32]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_abi_version.argtypes = []

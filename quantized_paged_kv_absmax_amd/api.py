@@ -71,7 +71,7 @@ def _out_torch_dtype(odt):
 def row_bytes(dtype, head_dim):
     d = _dt(dtype)
     return {_lib.BF16: 2 * head_dim, _lib.INT8: head_dim, _lib.FP8_E4M3: head_dim, _lib.FP8_E5M2: head_dim,
-            _lib.INT4_ASYM: head_dim // 2}[d]
+            _lib.INT4_ASYM: head_dim // 2, _lib.INT4_HAD: head_dim // 2}[d]
 
 
 class PagedKVCache:
@@ -87,8 +87,9 @@ class PagedKVCache:
                  v_gran="per_tensor", device="cuda", block_size=16, fill=0xFF):
         self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size = num_blocks, num_kv_heads, head_dim, block_size
         self.k_dtype, self.v_dtype = _dt(k_dtype), _dt(v_dtype)
-        self.k_gran = _lib.PER_TOKEN_HEAD if self.k_dtype == _lib.INT4_ASYM else _gr(k_gran)
-        self.v_gran = _lib.PER_TOKEN_HEAD if self.v_dtype == _lib.INT4_ASYM else _gr(v_gran)
+        int4 = (_lib.INT4_ASYM, _lib.INT4_HAD)
+        self.k_gran = _lib.PER_TOKEN_HEAD if self.k_dtype in int4 else _gr(k_gran)
+        self.v_gran = _lib.PER_TOKEN_HEAD if self.v_dtype in int4 else _gr(v_gran)
         shp = (num_blocks, num_kv_heads, block_size)
         self.k_pages = torch.full(shp + (row_bytes(self.k_dtype, head_dim),), fill, dtype=torch.uint8, device=device)
         self.v_pages = torch.full(shp + (row_bytes(self.v_dtype, head_dim),), fill, dtype=torch.uint8, device=device)
@@ -98,7 +99,7 @@ class PagedKVCache:
         self.k_absmax = torch.zeros_like(self.k_scale)
         self.v_absmax = torch.zeros_like(self.v_scale)
         meta = lambda dt: (torch.full(shp + (2,), float("nan"), dtype=torch.float32, device=device)
-                           if dt == _lib.INT4_ASYM else None)
+                           if dt in int4 else None)
         self.k_meta, self.v_meta = meta(self.k_dtype), meta(self.v_dtype)
 
     def struct(self, k_pages=None, v_pages=None):
@@ -161,6 +162,25 @@ def kvq_convert_cache(cache, k_src, v_src, first_block=0, num_blocks=None, strea
     check(st, "kvq_convert_cache")
 
 
+def kvq_hadamard_rotate(x, out=None, stream=None):
+    """bf16 rows x [..., D] -> bf16 rows of H x, the rotation of rotated-key (int4h) caches."""
+    _need(x, torch.bfloat16, "x")
+    D = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, torch.bfloat16, "out", shape=x.shape, device=x.device)
+    st = _lib.load().kvq_hadamard_rotate(_ptr(x), x.numel() // max(D, 1), D, _ptr(out), _stream(stream))
+    check(st, "kvq_hadamard_rotate")
+    return out
+
+
+def _query_for(cache, q, softmax_scale, stream):
+    """Rotated-key caches take the rotated query and the logit scale / D (H H = D I)."""
+    if cache.k_dtype != _lib.INT4_HAD:
+        return q, softmax_scale
+    return kvq_hadamard_rotate(q, stream=stream), float(softmax_scale) / cache.head_dim
+
+
 def kvq_verify_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition=0):
     return int(_lib.load().kvq_verify_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                                      partition))
@@ -200,6 +220,7 @@ def kvq_paged_attention_verify(cache, q, n_q, block_tables, seq_lens, max_seq_le
         _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
+    q, softmax_scale = _query_for(cache, q, softmax_scale, stream)
     st = _lib.load().kvq_paged_attention_verify(
         ctypes.byref(s), _ptr(q), int(n_q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
         int(max_seq_len), Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out),
@@ -256,6 +277,7 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
         _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
+    q, softmax_scale = _query_for(cache, q, softmax_scale, stream)
     st = _lib.load().kvq_paged_attention_decode(
         ctypes.byref(s), _ptr(q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
         Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out), _ptr(err_count),

@@ -99,6 +99,35 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
   *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
 }
 
+// The unnormalised Walsh-Hadamard transform of a row held by LPR aligned lanes,
+// 8 values each (x[i] = element 8 j + i): stages h = 1, 2, 4 inside the lane,
+// then h = 8 .. D/2 between lanes j and j ^ (h / 8); the pair at (i, i + h)
+// becomes (a + b, a - b) in float32, stage by stage in increasing h, and the
+// result is rounded to bf16 (returned as float32).
+template <int LPR>
+__device__ __forceinline__ void hadamard_row(float (&x)[8], int j) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & h)) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    const bool upper = j & m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float other = __shfl_xor(x[i], m, 64);
+      x[i] = upper ? other - x[i] : x[i] + other;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(f32_to_bf16_bits(x[i]));
+}
+
 // this lane's 16 source bytes of a row, and the row's scale
 struct RowIn {
   uint4 raw;
@@ -128,8 +157,13 @@ __device__ __forceinline__ void store_row(const RowSide& sd, const RowIn& in, in
     x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
     x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
   }
-  const int rb = (sd.dtype == DT_INT4) ? D / 2 : D;
-  encode_store<D, LPR>(x, sd.dtype, in.s, sd.pages + dst_row_idx * rb,
+  int dt = sd.dtype;
+  if (dt == DT_INT4H) {   // uniform per launch side: every lane of the row takes it
+    hadamard_row<LPR>(x, j);
+    dt = DT_INT4;
+  }
+  const int rb = (dt == DT_INT4) ? D / 2 : D;
+  encode_store<D, LPR>(x, dt, in.s, sd.pages + dst_row_idx * rb,
                        sd.meta ? sd.meta + dst_row_idx * 2 : nullptr, j);
 }
 
@@ -181,6 +215,29 @@ __global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v,
   store_row<D>(sd, load_row<D>(sd, sd.src + dst * D, h, j), dst, j);
 }
 
+template <int D>
+__global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t* x, int64_t rows, uint16_t* out) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;
+  const int j = threadIdx.x % LPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  if (r >= rows) return;   // whole rows: a row's lanes leave together
+  const uint4 raw = *reinterpret_cast<const uint4*>(x + r * D + 8 * j);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+  hadamard_row<LPR>(v, j);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + r * D + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 RowSide side(const CacheView& c, bool is_k, const uint16_t* src) {
   RowSide s;
   s.src = src;
@@ -218,6 +275,15 @@ hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const u
       hipLaunchKernelGGL((cache_write_kernel<64, false>), grid, dim3(kThreads), 0, s, k, v, slots, T,
                          c.num_kv_heads, num_slots, err);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard(const uint16_t* x, int64_t rows, int D, uint16_t* out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int rpb = kThreads / (D / 8);
+  dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+  if (D == 128) hipLaunchKernelGGL(hadamard_kernel<128>, grid, dim3(kThreads), 0, s, x, rows, out);
+  else hipLaunchKernelGGL(hadamard_kernel<64>, grid, dim3(kThreads), 0, s, x, rows, out);
   return hipGetLastError();
 }
 

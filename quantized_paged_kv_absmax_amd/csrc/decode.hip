@@ -7,6 +7,7 @@ namespace kvq {
 
 bool decode_supported(int kt, int vt, int D) {
   if (D != 64 && D != 128) return false;
+  if (kt == DT_INT4H) kt = DT_INT4;   // rotated keys: the same codes and kernels
   if (kt == DT_INT4 || vt == DT_INT4) return kt == DT_INT4 && vt == DT_INT4;
   const auto ok = [](int t) { return t == DT_BF16 || t == DT_INT8 || t == DT_E4M3 || t == DT_E5M2; };
   return ok(kt) && ok(vt);
@@ -52,9 +53,11 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   const int groups = (prm.n_tiles + prm.wg_waves - 1) / prm.wg_waves;   // workgroups per (chunk, KV head)
   dim3 grid(a.n_chunks * groups, c.num_kv_heads);
   hipError_t e;
-  if (a.n_q > 1) e = launch_chunk_verify(prm, c.k_dtype, c.v_dtype, c.head_dim, grid, s);
-  else e = (c.head_dim == 128) ? launch_kv<128, false>(c.k_dtype, c.v_dtype, prm, grid, s)
-                               : launch_kv<64, false>(c.k_dtype, c.v_dtype, prm, grid, s);
+  // rotated keys (DT_INT4H) are INT4 codes: the caller rotated the query alike
+  const int kt = (c.k_dtype == DT_INT4H) ? DT_INT4 : c.k_dtype;
+  if (a.n_q > 1) e = launch_chunk_verify(prm, kt, c.v_dtype, c.head_dim, grid, s);
+  else e = (c.head_dim == 128) ? launch_kv<128, false>(kt, c.v_dtype, prm, grid, s)
+                               : launch_kv<64, false>(kt, c.v_dtype, prm, grid, s);
   if (e != hipSuccess || a.ws_rec == nullptr) return e;
   // many rows with few pieces each (several query tokens, a large batch): a lane
   // group per row; else a workgroup per row, its groups splitting the pieces

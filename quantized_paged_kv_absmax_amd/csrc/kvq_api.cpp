@@ -22,13 +22,15 @@ constexpr int kMinChunk = 4;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_store_dtype(int32_t d) {
-  return d == KVQ_BF16 || d == KVQ_INT8 || d == KVQ_FP8_E4M3 || d == KVQ_FP8_E5M2 || d == KVQ_INT4_ASYM;
+  return d == KVQ_BF16 || d == KVQ_INT8 || d == KVQ_FP8_E4M3 || d == KVQ_FP8_E5M2 || d == KVQ_INT4_ASYM ||
+         d == KVQ_INT4_HAD;
 }
 
 // Checks shared by every call that takes a cache.
 kvq_status check_cache(const kvq_cache* c) {
   if (!c) return KVQ_ERR_NULL;
   if (!valid_store_dtype(c->k_dtype) || !valid_store_dtype(c->v_dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (c->v_dtype == KVQ_INT4_HAD) return KVQ_ERR_UNSUPPORTED;   // rotated rows are keys only
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   if (c->block_size != 16) return KVQ_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_blocks < 0) return KVQ_ERR_SHAPE;
@@ -39,7 +41,7 @@ kvq_status check_cache(const kvq_cache* c) {
   const float* scales[2] = {c->k_scale, c->v_scale};
   const float* metas[2] = {c->k_meta, c->v_meta};
   for (int i = 0; i < 2; ++i) {
-    if (dts[i] == KVQ_INT4_ASYM) {
+    if (dts[i] == KVQ_INT4_ASYM || dts[i] == KVQ_INT4_HAD) {
       if (grs[i] != KVQ_PER_TOKEN_HEAD) return KVQ_ERR_UNSUPPORTED;
       if (!metas[i]) return KVQ_ERR_NULL;
       if (!aligned16(metas[i])) return KVQ_ERR_ALIGN;
@@ -62,7 +64,8 @@ kvq::CacheView view(const kvq_cache* c) {
   v.head_dim = c->head_dim;
   v.k_pages = static_cast<uint8_t*>(c->k_pages);
   v.v_pages = static_cast<uint8_t*>(c->v_pages);
-  v.k_scale = c->k_dtype == KVQ_BF16 || c->k_dtype == KVQ_INT4_ASYM ? nullptr : c->k_scale;
+  v.k_scale = (c->k_dtype == KVQ_BF16 || c->k_dtype == KVQ_INT4_ASYM || c->k_dtype == KVQ_INT4_HAD) ? nullptr
+                                                                                                   : c->k_scale;
   v.v_scale = c->v_dtype == KVQ_BF16 || c->v_dtype == KVQ_INT4_ASYM ? nullptr : c->v_scale;
   v.k_meta = c->k_meta;
   v.v_meta = c->v_meta;
@@ -251,6 +254,18 @@ kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q,
   return from_hip(kvq::launch_decode(view(cache), a, static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_hadamard_rotate(const uint16_t* x, int64_t num_rows, int32_t head_dim, uint16_t* out,
+                               void* stream) {
+  if (head_dim != 64 && head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (num_rows < 0) return KVQ_ERR_SHAPE;
+  if (num_rows == 0) return KVQ_OK;
+  if (!x || !out) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  const int64_t rows_per_block = 256 / (head_dim / 8);
+  if ((num_rows + rows_per_block - 1) / rows_per_block > INT32_MAX) return KVQ_ERR_SHAPE;
+  return from_hip(kvq::launch_hadamard(x, num_rows, head_dim, out, static_cast<hipStream_t>(stream)));
+}
+
 const char* kvq_status_string(int32_t status) {
   switch (status) {
     case KVQ_OK: return "KVQ_OK";
@@ -270,7 +285,7 @@ uint64_t kvq_cache_block_bytes(int32_t k_dtype, int32_t v_dtype, int32_t num_kv_
   if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || (head_dim & 1)) return 0;
   auto row = [&](int32_t d) -> uint64_t {
     if (d == KVQ_BF16) return 2ull * head_dim;
-    if (d == KVQ_INT4_ASYM) return (uint64_t)head_dim / 2 + 8;   // codes + fp32 (scale, zero point)
+    if (d == KVQ_INT4_ASYM || d == KVQ_INT4_HAD) return (uint64_t)head_dim / 2 + 8;   // codes + fp32 (scale, zero point)
     return (uint64_t)head_dim;
   };
   return (row(k_dtype) + row(v_dtype)) * (uint64_t)num_kv_heads * (uint64_t)block_size;

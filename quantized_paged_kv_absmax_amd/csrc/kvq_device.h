@@ -20,7 +20,8 @@
 
 namespace kvq {
 
-enum : int { DT_BF16 = 0, DT_INT8 = 1, DT_E4M3 = 2, DT_E5M2 = 3, DT_INT4 = 4, DT_F32 = 5 };
+// DT_INT4H: INT4 codes of the Hadamard-rotated row (keys only)
+enum : int { DT_BF16 = 0, DT_INT8 = 1, DT_E4M3 = 2, DT_E5M2 = 3, DT_INT4 = 4, DT_F32 = 5, DT_INT4H = 6 };
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));

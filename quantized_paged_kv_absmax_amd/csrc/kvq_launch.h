@@ -25,6 +25,9 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int Hkv, int D, int pe
 hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const uint16_t* v_new,
                               const int64_t* slots, int64_t T, int32_t* err, hipStream_t s);
 
+// bf16 rows [rows][D] -> bf16 of their Hadamard transform (DT_INT4H's rotation)
+hipError_t launch_hadamard(const uint16_t* x, int64_t rows, int D, uint16_t* out, hipStream_t s);
+
 hipError_t launch_convert(const CacheView& c, const uint16_t* k_src, const uint16_t* v_src,
                           int first_block, int n_blocks, hipStream_t s);
 

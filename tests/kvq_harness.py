@@ -204,7 +204,7 @@ def assert_codes_equal(r, oracle_cache, inp, seqs=None):
         else:
             bad = g != e
         assert not bad.any(), f"{which}: {int(bad.sum())} code bytes differ (first at {np.argwhere(bad)[:3].tolist()})"
-        if dt == "int4":
+        if dt in ("int4", "int4h"):
             gm = pick(getattr(r.cache, which + "_meta"), False).transpose(0, 2, 1, 3)[vm]
             em = pick(getattr(oracle_cache, which + "_meta"), True).transpose(0, 2, 1, 3)[vm]
             assert np.array_equal(gm.view(np.uint32), em.view(np.uint32)), f"{which} int4 metadata differs"

@@ -19,7 +19,8 @@ def _write_rows(dtype, rows_bits, scale, gran="per_tensor", H=1):
     """Write rows [T][H][D] at slots 0..T-1 of a fresh cache; return pages (numpy) and meta."""
     T, H_, D = rows_bits.shape
     nb = -(-T // 16)
-    c = kvq.PagedKVCache(nb, H_, D, dtype, dtype, k_gran=gran, v_gran=gran)
+    vdt = "int4" if dtype == "int4h" else dtype        # rotated rows are keys only
+    c = kvq.PagedKVCache(nb, H_, D, dtype, vdt, k_gran=gran, v_gran=gran)
     if scale is not None:
         c.k_scale.copy_(torch.as_tensor(np.asarray(scale, np.float32).reshape(-1)))
         c.v_scale.copy_(torch.as_tensor(np.asarray(scale, np.float32).reshape(-1)))
@@ -70,10 +71,26 @@ def test_int4_rows(D):
     x[2::50] = 3.25                        # constant rows
     x[3::50] = 0.0
     bits = (x.view(np.uint32) >> 16).astype(np.uint16)
-    got, gm = _write_rows("int4", bits, None)
-    ref, rm = oc.encode_rows(bits, "int4")
-    assert np.array_equal(got, ref)
-    assert np.array_equal(gm.view(np.uint32), rm.view(np.uint32))
+    for dt in ("int4", "int4h"):
+        got, gm = _write_rows(dt, bits, None)
+        ref, rm = oc.encode_rows(bits, dt)
+        assert np.array_equal(got, ref), dt
+        assert np.array_equal(gm.view(np.uint32), rm.view(np.uint32)), dt
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_rotate_bit_exact(D):
+    """kvq_hadamard_rotate against the oracle's float32 butterfly: normal rows,
+    rows with wide magnitude spreads (rounding in every stage), a row near the
+    bf16 maximum (sums overflow to inf) and zero rows."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((777, D)).astype(np.float32)
+    x[::7] *= np.float32(2.0) ** rng.integers(-30, 30, size=(x[::7].shape[0], D)).astype(np.float32)
+    x[3] = 3.0e38
+    x[4] = 0.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    got = kvq.kvq_hadamard_rotate(dev_bf16(bits)).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, codecs.hadamard_rotate_bf16(bits))
 
 
 def test_bf16_copy_and_slot_errors():
@@ -120,7 +137,7 @@ def test_calibrate_bit_exact(D):
     assert s.item() == 1.0 and a.item() == 0.0
 
 
-@pytest.mark.parametrize("dst", [("int4", "int4"), ("int8", "e4m3")])
+@pytest.mark.parametrize("dst", [("int4", "int4"), ("int8", "e4m3"), ("int4h", "int4")])
 def test_convert_bit_exact(dst):
     rng = np.random.default_rng(5)
     nb, H, D = 37, 8, 128
@@ -129,9 +146,10 @@ def test_convert_bit_exact(dst):
     kb = (x.view(np.uint32) >> 16).astype(np.uint16)
     vb = ((x * 0.5).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     c = kvq.PagedKVCache(nb, H, D, dst[0], dst[1])
-    o = oc.PagedCache(nb, H, D, dst[0], dst[1], k_scale=np.float32(0.05) if dst[0] != "int4" else None,
-                      v_scale=np.float32(0.003) if dst[1] != "int4" else None)
-    if dst[0] != "int4":
+    i4 = ("int4", "int4h")
+    o = oc.PagedCache(nb, H, D, dst[0], dst[1], k_scale=np.float32(0.05) if dst[0] not in i4 else None,
+                      v_scale=np.float32(0.003) if dst[1] not in i4 else None)
+    if dst[0] not in i4:
         c.k_scale.fill_(0.05)
         c.v_scale.fill_(0.003)
     kvq.kvq_convert_cache(c, dev_bf16(kb), dev_bf16(vb), 3, 30)
@@ -139,6 +157,6 @@ def test_convert_bit_exact(dst):
     torch.cuda.synchronize()
     assert np.array_equal(c.k_pages.cpu().numpy(), o.k_pages)
     assert np.array_equal(c.v_pages.cpu().numpy(), o.v_pages)
-    if dst[0] == "int4":
+    if dst[0] in i4:
         assert np.array_equal(c.k_meta.cpu().numpy().view(np.uint32), o.k_meta.view(np.uint32))
         assert np.array_equal(c.v_meta.cpu().numpy().view(np.uint32), o.v_meta.view(np.uint32))

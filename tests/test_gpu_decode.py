@@ -25,6 +25,7 @@ CASES = {
     "fp8_e5m2_cal": dict(B=6),
     "longctx_int8": dict(B=2, lens=("uniform", 1000, 3000)),
     "int4": dict(B=8, lens=("uniform", 20, 1500)),
+    "int4_had": dict(B=8, lens=("uniform", 20, 1500)),
     "bf16": dict(B=6, lens=("uniform", 20, 1500)),
 }
 

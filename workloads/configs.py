@@ -25,6 +25,8 @@ block_size 16):
                  sequences; every (K or V, head, channel) has its own standard
                  deviation drawn once from LogNormal(0, 0.5); decoded with
                  512-token work chunks (32 pages) and the merge pass.
+  int4_had       as int4, with the keys Hadamard-rotated before their INT4 codes
+                 (KVarN's rotation step); the query is rotated alike.
   int4           B=128, lengths U[1024, 8192], 32/8/128, INT4 asymmetric per
                  (token, KV head); K channels as above, V plain N(0,1); the cache
                  starts as bf16 pages and is converted.
@@ -109,6 +111,11 @@ WORKLOADS = {
                      k_scale_mode="row", v_scale_mode="row",
                      k_outliers=_outliers(8, 128, 0.01), calib="none", new_tokens=0,
                      from_bf16_cache=True),
+    "int4_had": Workload("int4_had", 9, 128, 32, 8, 128, ("uniform", 1024, 8192), "int4h", "int4",
+                         k_gran="per_token_head", v_gran="per_token_head",
+                         k_scale_mode="row", v_scale_mode="row",
+                         k_outliers=_outliers(8, 128, 0.01), calib="none", new_tokens=0,
+                         from_bf16_cache=True),
     "bf16": Workload("bf16", 2, 64, 32, 8, 128, ("uniform", 512, 4096), "bf16", "bf16",
                      k_scale_mode="one", v_scale_mode="one",
                      k_outliers=_outliers(8, 128, 0.01), calib="none", new_tokens=1),
