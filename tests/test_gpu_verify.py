@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 def _small(kd, vd, Hq, Hkv, D, n_q, lens, seed=31):
     w = WORKLOADS["tiny_int8"].with_(B=len(lens), lens=("fixed", lens), Hq=Hq, Hkv=Hkv, D=D, k_dtype=kd,
                                      v_dtype=vd, seed=seed, n_q=n_q, new_tokens=0, calib="all")
-    if kd == "int4":
+    if kd in ("int4", "int4h"):
         w = w.with_(k_gran="per_token_head", v_gran="per_token_head", k_scale_mode="row", v_scale_mode="row",
                     calib="none")
     elif kd == "bf16":
@@ -32,6 +32,7 @@ CASES = [
     ("int8", "int8", 8, 2, 128, 16),
     ("e4m3", "e5m2", 6, 2, 128, 7),
     ("int4", "int4", 16, 2, 128, 5),
+    ("int4h", "int4", 8, 2, 128, 16),      # rotated keys: the query rows rotated alike
     ("bf16", "bf16", 16, 1, 64, 3),
     ("e4m3", "int8", 2, 2, 64, 20),
     ("int8", "e4m3", 8, 2, 128, 64),      # a prefill chunk: 16 tiles, 4 workgroups per (chunk, KV head)
