@@ -208,3 +208,27 @@ def test_binding_rejects_host_tensors():
         kvq.kvq_calibrate_scales(x, "per_tensor", "int8", c.k_absmax, c.k_scale)
     with pytest.raises(TypeError):
         kvq.kvq_cache_write(c, x.float(), x, torch.arange(3))
+
+
+def test_rotated_key_format_argument_errors():
+    """KVQ_INT4_HAD is a key format (INT4 layout, metadata required) and
+    kvq_hadamard_rotate checks its arguments before any launch."""
+    lib = _lib.load()
+    tok = dict(k_dtype=_lib.INT4_HAD, v_dtype=_lib.INT4_ASYM, k_gran=_lib.PER_TOKEN_HEAD,
+               v_gran=_lib.PER_TOKEN_HEAD, k_meta=FAKE, v_meta=FAKE)
+    c = _cache(**tok)
+    assert lib.kvq_cache_write(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None, None) == _lib.OK
+    bad_v = _cache(**dict(tok, v_dtype=_lib.INT4_HAD))
+    assert lib.kvq_cache_write(ctypes.byref(bad_v), FAKE, FAKE, FAKE, 0, None, None) == _lib.ERR_UNSUPPORTED
+    no_meta = _cache(**dict(tok, k_meta=None))
+    assert lib.kvq_cache_write(ctypes.byref(no_meta), FAKE, FAKE, FAKE, 0, None, None) == _lib.ERR_NULL
+    per_tensor = _cache(**dict(tok, k_gran=_lib.PER_TENSOR))
+    assert lib.kvq_cache_write(ctypes.byref(per_tensor), FAKE, FAKE, FAKE, 0, None, None) == _lib.ERR_UNSUPPORTED
+    assert lib.kvq_cache_block_bytes(_lib.INT4_HAD, _lib.INT4_ASYM, 8, 128, 16) == \
+        lib.kvq_cache_block_bytes(_lib.INT4_ASYM, _lib.INT4_ASYM, 8, 128, 16)
+    assert lib.kvq_hadamard_rotate(FAKE, 4, 96, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert lib.kvq_hadamard_rotate(FAKE, -1, 128, FAKE, None) == _lib.ERR_SHAPE
+    assert lib.kvq_hadamard_rotate(FAKE, 0, 128, FAKE, None) == _lib.OK
+    assert lib.kvq_hadamard_rotate(None, 4, 128, FAKE, None) == _lib.ERR_NULL
+    assert lib.kvq_hadamard_rotate(FAKE, 4, 64, None, None) == _lib.ERR_NULL
+    assert lib.kvq_hadamard_rotate(FAKE + 2, 4, 64, FAKE, None) == _lib.ERR_ALIGN
