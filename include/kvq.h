@@ -214,7 +214,8 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
  *   out_dtype     KVQ_BF16 (round to nearest even) or KVQ_F32
  *   out           (device) [batch][num_q_heads][head_dim] of out_dtype
  * Supported K/V dtype pairs: any of {INT8, FP8_E4M3, FP8_E5M2, BF16} for K and for
- * V independently, and INT4 for both.
+ * V independently, INT4 for both, and KVQ_INT4_HAD keys with INT4 values (q then
+ * rotated by kvq_hadamard_rotate and softmax_scale divided by head_dim).
  */
 kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
