@@ -23,9 +23,10 @@ Several query tokens per sequence (``verify``): token i of the last n_q
 positions attends causally to positions 0..L_b - n_q + i.
 
 Rotated keys (K dtype "int4h", KVarN's rotation step, techfi24's KVarN article,
-"Contexte Technique"): the cache holds INT4 codes of H k; the query is rotated
-the same way (H q, rounded to bf16 as the caller hands it over) and the logit
-scale is divided by D, since (H q) . (H k) = D (q . k).
+"Contexte Technique"): the cache holds INT4 codes of H k (H the Sylvester-Hadamard
+matrix, H H = D I).  The key such a slot holds is the de-rotated row
+k_hat = H k_hat_rot / D, and attention is the plain formula above over those keys
+with the caller's query and softmax scale as given.
 
 Pins (tests/test_oracle_attention.py): q = 0 gives the mean of v_hat; one
 token gives v_hat_0; adding a constant to every logit changes nothing; a
@@ -39,13 +40,15 @@ import numpy as np
 from . import codecs
 
 
-def _rotated_query(cache, q_bits):
-    """Rotated-key caches take H q (bf16), others q itself."""
-    return codecs.hadamard_rotate_bf16(q_bits) if cache.k_dtype == "int4h" else q_bits
-
-
-def _logit_divisor(cache):
-    return cache.D if cache.k_dtype == "int4h" else 1
+def _keys(cache, block_table_row, L, heads=None):
+    """Dequantised keys of one sequence's first L positions, float64 [L][h][D].
+    A rotated-key ("int4h") slot holds H k; its key is H (H k) / D, taken in
+    float64 (a product of at most 128 float32 terms per element)."""
+    K = cache.gather(block_table_row, L, "k", heads).astype(np.float64)
+    if cache.k_dtype == "int4h":
+        H = codecs.hadamard_matrix(cache.D).astype(np.float64)
+        K = (K @ H.T) / cache.D
+    return K
 
 
 def _attend(qv, K, V, softmax_scale):
@@ -64,11 +67,10 @@ def decode(cache, q_bits, block_tables, seq_lens, softmax_scale, heads=None, seq
     caller passes (used exactly).  ``heads`` / ``seqs`` restrict the work to a
     subset (other rows are left NaN), for sampled checks at large sizes.
     """
-    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     B, Hq, D = q.shape
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
+    sm = float(np.float32(softmax_scale))
     out = np.full((B, Hq, D), np.nan)
     for b in (range(B) if seqs is None else seqs):
         L = int(seq_lens[b])
@@ -78,7 +80,7 @@ def decode(cache, q_bits, block_tables, seq_lens, softmax_scale, heads=None, seq
                 out[b, h] = 0.0
             continue
         kvs = sorted({h // g for h in hs})
-        K = cache.gather(block_tables[b], L, "k", kvs).astype(np.float64)   # [L][len(kvs)][D]
+        K = _keys(cache, block_tables[b], L, kvs)                         # [L][len(kvs)][D]
         V = cache.gather(block_tables[b], L, "v", kvs).astype(np.float64)
         col = {kv: i for i, kv in enumerate(kvs)}
         for h in hs:
@@ -101,12 +103,11 @@ def verify(cache, q_bits, n_q, block_tables, seq_lens, softmax_scale, heads=None
     p < 0 (a sequence shorter than n_q) gives a zero row.  ``heads`` / ``seqs``
     restrict the work (other rows NaN).
     """
-    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     T, Hq, D = q.shape
     B = T // n_q
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
+    sm = float(np.float32(softmax_scale))
     out = np.full((T, Hq, D), np.nan)
     for b in (range(B) if seqs is None else seqs):
         L = int(seq_lens[b])
@@ -114,7 +115,7 @@ def verify(cache, q_bits, n_q, block_tables, seq_lens, softmax_scale, heads=None
         kvs = sorted({h // g for h in hs})
         col = {kv: i for i, kv in enumerate(kvs)}
         if L > 0:
-            K = cache.gather(block_tables[b], L, "k", kvs).astype(np.float64)
+            K = _keys(cache, block_tables[b], L, kvs)
             V = cache.gather(block_tables[b], L, "v", kvs).astype(np.float64)
         for i in range(n_q):
             t, pos = b * n_q + i, L - n_q + i
@@ -134,11 +135,10 @@ def decode_partials(cache, q_bits, block_tables, seq_lens, softmax_scale, partit
     partitions of the longest sequence.  Partitions with no tokens hold
     m = -inf, l = 0, acc = 0.
     """
-    q_bits = _rotated_query(cache, q_bits)
     q = codecs.bf16_to_f32(np.asarray(q_bits, np.uint16)).astype(np.float64)
     B, Hq, D = q.shape
     g = Hq // cache.H
-    sm = float(np.float32(softmax_scale)) / _logit_divisor(cache)
+    sm = float(np.float32(softmax_scale))
     Lmax = max(int(x) for x in seq_lens) if len(seq_lens) else 0
     P = max(1, -(-Lmax // partition))
     m = np.full((B, Hq, P), -np.inf)
@@ -148,7 +148,7 @@ def decode_partials(cache, q_bits, block_tables, seq_lens, softmax_scale, partit
         L = int(seq_lens[b])
         if L <= 0:
             continue
-        K = cache.gather(block_tables[b], L, "k").astype(np.float64)
+        K = _keys(cache, block_tables[b], L)
         V = cache.gather(block_tables[b], L, "v").astype(np.float64)
         for h in range(Hq):
             z = sm * (K[:, h // g, :] @ q[b, h])

@@ -19,10 +19,16 @@ Pins (tests/test_oracle_codecs.py):
                       constant rows, hand-packed nibble order.
   kv_bytes_per_token_head - the 2.00x GPU-block ratios printed in the L4 table
                       of vLLM PR 4893 (FP16 vs FP8 KV at equal memory).
-  hadamard_rotate_bf16 - scipy's Sylvester Hadamard matrix in float64 (exact on
-                      integer rows, within the bf16 rounding otherwise), H H = D I,
-                      the closed-form columns (-1)^popcount(i & k), and preserved
-                      dot products.
+  hadamard_rotate_bf16 - scipy's Sylvester Hadamard matrix (library routine) in
+                      float64 on rows whose products are exact there, with torch's
+                      float32 -> bf16 rounding of results exact in float32; a
+                      brute-force nearest-bf16 search (ties to even) on exact
+                      rational results, including halfway cases, subnormals and
+                      overflow; H H = D I; preserved dot products; IEEE infinity
+                      and NaN rules.
+  fp8_is_nan_code   - torch's float8_e4m3fn / float8_e5m2 isnan over all codes.
+  f32_to_bf16_rne   - torch's float32 -> bfloat16 cast on random values, exact
+                      ties, overflow and NaN.
 """
 
 import numpy as np
@@ -221,11 +227,14 @@ def int4_row_params(x):
         if s == 0 or s is not finite:  s = |mn| if mn != 0 else 1.0
         zp = RNE(fl32(-mn / s))                 (an integer held in float32,
                                                  not clamped)
+    NaN elements are left out of min and max (fmin / fmax, as the calibration
+    does); a row of only NaNs gets (NaN, NaN).
     Returns (s, zp), float32 arrays over the leading axes.
     """
     x = np.asarray(x, dtype=F32)
-    mn = x.min(axis=-1)
-    mx = x.max(axis=-1)
+    with np.errstate(invalid="ignore"):
+        mn = np.fmin.reduce(x, axis=-1)       # NaN elements are left out (a row
+        mx = np.fmax.reduce(x, axis=-1)       # of only NaNs gives NaN)
     with np.errstate(over="ignore", invalid="ignore"):
         rng = np.subtract(mx, mn, dtype=F32)
         s = np.divide(rng, F32(15.0), dtype=F32)
@@ -240,12 +249,15 @@ def int4_encode_rows(x):
     """INT4 codes of float32 rows ``x`` [..., D]: returns (codes uint8 [..., D], s, zp).
 
     q = clamp(RNE(fl32(x / s)) + zp, 0, 15); the zero point is added after
-    rounding, as an integer.
+    rounding, as an integer.  A NaN element (or any element of an all-NaN row)
+    gets code 0, as the clamp's lower bound does for an unordered value.
     """
     x = np.asarray(x, dtype=F32)
     s, zp = int4_row_params(x)
-    t = _div32(x, s[..., None])
-    q = np.clip(np.rint(t) + zp[..., None], 0, 15)
+    with np.errstate(invalid="ignore"):
+        t = _div32(x, s[..., None])
+        q = np.clip(np.rint(t) + zp[..., None], 0, 15)
+    q = np.where(np.isnan(q), 0, q)
     return q.astype(np.uint8), s, zp
 
 
@@ -279,29 +291,162 @@ def int4_decode(codes, s, zp):
 # ---------------------------------------------------------------------------
 # Hadamard rotation of a row (the rotation step of KVarN: techfi24's KVarN
 # article, "Contexte Technique").  Reading: the unnormalised Sylvester-Hadamard
-# transform of the row's D values, H x with H[i][k] = (-1)^popcount(i & k), taken
-# in float32 by the fast Walsh-Hadamard butterfly (stages h = 1, 2, 4, ..., D/2;
-# the pair at indices (i, i + h), i & h == 0, becomes (a + b, a - b)) and rounded
-# to bf16.  H H = D I, so (H q) . (H k) = D (q . k): the logit scale takes 1 / D.
+# transform of the row's D values, y = H x with H[i][k] = (-1)^popcount(i & k),
+# computed exactly and rounded once to bf16 (round to nearest, ties to even).
+# H H = D I, so a key stored as H k is recovered as H (H k) / D.
 # ---------------------------------------------------------------------------
+
+BF16_MIN_LSB_EXP = -133      # exponent of the smallest bf16 subnormal, 2^-133
+BF16_MAX_EXP = 127           # largest binade of a finite bf16 (values < 2^128)
+
+
+def hadamard_matrix(D):
+    """The Sylvester-Hadamard matrix of order D (a power of two), from its closed
+    form H[i][k] = (-1)^popcount(i & k), as int64."""
+    assert D > 0 and D & (D - 1) == 0
+    i = np.arange(D, dtype=np.int64)
+    a = i[:, None] & i[None, :]
+    pop = np.zeros_like(a)
+    while a.any():
+        pop += a & 1
+        a >>= 1
+    return np.where(pop % 2 == 0, 1, -1).astype(np.int64)
+
+
+def _round_int_to_bf16(Y, e0):
+    """bf16 bits of the exact value Y * 2^e0 (Y a Python int), round to nearest,
+    ties to even, overflowing to +-Inf; an exact zero gives +0."""
+    if Y == 0:
+        return 0
+    sign = 0x8000 if Y < 0 else 0
+    A = -Y if Y < 0 else Y
+    msb = A.bit_length() - 1 + e0                   # exponent of the leading bit
+    qe = max(msb - 7, BF16_MIN_LSB_EXP)             # exponent of the result's last bit
+    sh = qe - e0
+    if sh <= 0:
+        R = A << (-sh)
+    else:
+        R = A >> sh
+        rem = A - (R << sh)
+        half = 1 << (sh - 1)
+        if rem > half or (rem == half and (R & 1)):
+            R += 1
+    # R * 2^qe with R <= 256: renormalise a carry out of the top bit
+    if R == 256:
+        R, qe = 128, qe + 1
+    if R == 0:
+        return sign
+    if R >= 128:                                    # normal: R = 1.mmmmmmm * 2^7
+        e = qe + 7
+        if e > BF16_MAX_EXP:
+            return sign | 0x7F80
+        return sign | ((e + 127) << 7) | (R & 0x7F)
+    return sign | R                                 # subnormal: qe == -133
+
+
+def _fwht_int64(X):
+    """H X over the last axis in exact integer arithmetic, by the fast
+    Walsh-Hadamard factorisation of H into log2(D) stages, each pairing (i, i + h)
+    into (a + b, a - b).  Integer sums are exact in any order, so this is the
+    matrix product itself; callers keep |X| small enough for int64."""
+    X = np.array(X, np.int64)
+    D = X.shape[-1]
+    h = 1
+    while h < D:
+        y = X.reshape(X.shape[:-1] + (D // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        X = y.reshape(X.shape)
+        h *= 2
+    return X
+
+
+def _round_int64_to_bf16(Y, e0):
+    """_round_int_to_bf16 over an int64 array Y (|Y| < 2^62) with exponents e0
+    broadcast against it, in integer arithmetic throughout."""
+    Y = np.asarray(Y, np.int64)
+    e0 = np.broadcast_to(np.asarray(e0, np.int64), Y.shape)
+    sign = np.where(Y < 0, 0x8000, 0).astype(np.int64)
+    A = np.abs(Y)
+    # bit length of A: frexp of the float64 value, corrected where the
+    # conversion rounded A up to the next power of two
+    _, n = np.frexp(A.astype(np.float64))
+    n = n.astype(np.int64)
+    n = np.where((n > 0) & ((A >> np.maximum(n - 1, 0)) == 0), n - 1, n)
+    msb = n - 1 + e0
+    qe = np.maximum(msb - 7, BF16_MIN_LSB_EXP)
+    sh = qe - e0
+    up_sh = np.clip(-sh, 0, 62)
+    dn_sh = np.clip(sh, 0, 62)
+    Rdn = A >> dn_sh
+    rem = A - (Rdn << dn_sh)
+    half = np.where(dn_sh > 0, np.int64(1) << np.maximum(dn_sh - 1, 0), 0)
+    rup = (dn_sh > 0) & ((rem > half) | ((rem == half) & ((Rdn & 1) == 1)))
+    R = np.where(sh <= 0, A << up_sh, Rdn + rup)
+    carry = R == 256
+    R = np.where(carry, 128, R)
+    qe = np.where(carry, qe + 1, qe)
+    e = qe + 7
+    normal = R >= 128
+    bits = np.where(normal, ((e + 127) << 7) | (R & 0x7F), R)
+    bits = np.where(normal & (e > BF16_MAX_EXP), 0x7F80, bits)
+    bits = np.where(A == 0, 0, bits | sign)
+    return bits.astype(np.uint16)
 
 
 def hadamard_rotate_bf16(x_bits):
-    """bf16 rows [..., D] (D a power of two) -> bf16 bits of H x, as above."""
-    x = bf16_to_f32(np.asarray(x_bits, np.uint16)).astype(F32).copy()
-    D = x.shape[-1]
+    """bf16 rows [..., D] (D a power of two) -> bf16 bits of y = H x, as above.
+
+    Every finite bf16 value is an integer multiple of 2^-133, so with e0 the
+    smallest exponent of a last significand bit in the row, X_i = x_i / 2^e0
+    is an integer and y_j = 2^e0 * sum_i H[j][i] X_i is evaluated exactly in
+    integer arithmetic (int64 where the row's magnitudes allow it, Python
+    integers otherwise), then rounded once.  Non-finite rows: a NaN anywhere
+    makes every output NaN (0x7FC0); otherwise an output whose signed terms
+    hold both +Inf and -Inf is NaN, one holding only one sign of infinity is
+    that infinity.
+    """
+    bits = np.asarray(x_bits, np.uint16)
+    D = bits.shape[-1]
     assert D & (D - 1) == 0
-    lead = x.shape[:-1]
-    h = 1
-    while h < D:
-        y = x.reshape(lead + (D // (2 * h), 2, h))
-        a = y[..., 0, :].copy()
-        b = y[..., 1, :].copy()
-        y[..., 0, :] = a + b          # float32 arithmetic, round to nearest even
-        y[..., 1, :] = a - b
-        x = y.reshape(lead + (D,))
-        h *= 2
-    return f32_to_bf16_rne(x)
+    lead = bits.shape[:-1]
+    b = bits.reshape(-1, D).astype(np.int64)
+    H = hadamard_matrix(D)
+    E8 = (b >> 7) & 0xFF
+    man = b & 0x7F
+    fin = E8 != 0xFF
+    sig = np.where(E8 != 0, man | 0x80, man)                 # integer significand
+    sig = np.where(fin, sig, 0)
+    sig = np.where((b >> 15) == 1, -sig, sig)
+    lsb = np.maximum(E8, 1) - 127 - 7                        # exponent of the last bit
+    nz = sig != 0
+    e0 = np.where(nz, lsb, 10 ** 6).min(axis=1)
+    e0 = np.where(nz.any(axis=1), e0, 0)
+    spread = np.where(nz, lsb - e0[:, None], 0).max(axis=1)
+    out = np.zeros(b.shape, np.uint16)
+    # int64 fast path: |X_i| < 2^(spread + 8), sums of D terms below 2^62
+    fast = spread + 8 + int(np.log2(D)) <= 62
+    rows = np.nonzero(fast)[0]
+    if rows.size:
+        X = sig[rows] << (lsb[rows] - e0[rows, None]) * nz[rows]
+        Y = _fwht_int64(X)                                   # exact int64 sums
+        out[rows] = _round_int64_to_bf16(Y, e0[rows, None])
+    for r in np.nonzero(~fast)[0]:
+        X = [int(s) << int(l - e0[r]) if s else 0 for s, l in zip(sig[r], lsb[r])]
+        out[r] = [_round_int_to_bf16(sum(int(H[j, i]) * X[i] for i in range(D)), int(e0[r])) for j in range(D)]
+    # non-finite inputs
+    for r in np.nonzero((~fin).any(axis=1))[0]:
+        if (~fin[r] & (man[r] != 0)).any():
+            out[r] = 0x7FC0
+            continue
+        pos_inf = (~fin[r] & ((b[r] >> 15) == 0)).astype(np.int64)
+        neg_inf = (~fin[r] & ((b[r] >> 15) == 1)).astype(np.int64)
+        has_pos = ((H > 0) @ pos_inf + (H < 0) @ neg_inf) > 0      # y_j's terms that are +Inf
+        has_neg = ((H < 0) @ pos_inf + (H > 0) @ neg_inf) > 0      # ... and -Inf
+        out[r] = np.where(has_pos & has_neg, 0x7FC0,
+                          np.where(has_pos, 0x7F80, np.where(has_neg, 0xFF80, out[r])))
+    return out.reshape(lead + (D,))
 
 
 INT4_META_BYTES = 8  # float32 scale + float32 zero point per (token, KV head)

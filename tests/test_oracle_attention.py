@@ -190,26 +190,31 @@ def test_verify_zero_query_gives_prefix_mean():
 
 
 def test_rotated_keys_equal_derotated_attention():
-    """An "int4h" cache stores INT4 codes of H k; its decode rotates q and divides
-    the logit scale by D.  De-rotating the stored keys (H^-1 = H / D) must then
-    give the same attention with the plain query: catches a missing 1 / D, an
-    unrotated or differently rotated query."""
+    """An "int4h" cache stores INT4 codes of H k; its decode attends with the
+    de-rotated keys H k_hat_rot / D and the query as given.  The same logits come
+    from the other side of the identity, (H q) . k_hat_rot / D: torch's
+    scaled_dot_product_attention in float64 over the stored rows with the
+    rotated query (scipy's Hadamard matrix) and the scale divided by D.  A
+    missing 1 / D, an unrotated or transposed rotation fails it."""
     from scipy.linalg import hadamard
     inp = _inputs(B=2, lens=("fixed", (9, 40)), Hq=4, Hkv=2, D=64)
     c = oc.PagedCache(inp.num_blocks, 2, 64, "int4h", "int4")
     c.write(inp.k_bits, inp.v_bits, inp.slot_mapping)
     rng = np.random.default_rng(14)
-    q = rng.integers(-2, 3, size=inp.q_bits.shape).astype(np.float32)   # rotation exact in bf16
+    q = rng.standard_normal(inp.q_bits.shape).astype(np.float32)
     q_bits = codecs.f32_to_bf16_rne(q)
     out = oa.decode(c, q_bits, inp.block_tables, inp.seq_lens, 0.125)
+    qf = codecs.bf16_to_f32(q_bits).astype(np.float64)
     H = hadamard(64).astype(np.float64)
     for b in range(2):
         L = int(inp.seq_lens[b])
-        Kr = c.gather(inp.block_tables[b], L, "k").astype(np.float64)        # H k, dequantised
+        Kr = c.gather(inp.block_tables[b], L, "k").astype(np.float64)        # the stored rows: H k, dequantised
         V = c.gather(inp.block_tables[b], L, "v").astype(np.float64)
-        K = Kr @ H / 64.0                                                   # H symmetric, H H = 64 I
+        hq = qf[b] @ H.T                                                    # H q per head
         for h in range(4):
-            ref = oa._attend(q[b, h].astype(np.float64), K[:, h // 2, :], V[:, h // 2, :], 0.125)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(hq[h][None, None, None, :]), torch.from_numpy(Kr[None, None, :, h // 2, :]),
+                torch.from_numpy(V[None, None, :, h // 2, :]), scale=0.125 / 64).numpy()[0, 0, 0]
             np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
     # and the stored codes are those of the rotated rows
     plain = oc.PagedCache(inp.num_blocks, 2, 64, "int4", "int4")

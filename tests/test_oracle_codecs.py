@@ -256,20 +256,137 @@ def _bf16_bits(x):
     return codecs.f32_to_bf16_rne(np.asarray(x, np.float32))
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_hadamard_matches_sylvester_matrix(D):
+ALL_BF16_BITS = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+_FIN = ALL_BF16_BITS[((ALL_BF16_BITS >> 7) & 0xFF) != 0xFF]
+_FIN_VALS = codecs.bf16_to_f32(_FIN).astype(np.float64)
+
+
+def _nearest_bf16_brute(y):
+    """bf16 bits nearest to the exact rational y (a Fraction), found by search
+    over every finite bf16 value; ties go to the pattern with an even last
+    mantissa bit; at or beyond the halfway point above the largest finite
+    value, +-Inf.  Zero gives +0."""
+    if y == 0:
+        return 0
+    big = Fraction(2) ** 128 - Fraction(2) ** 119      # halfway between the largest finite and 2^128
+    if y >= big:
+        return 0x7F80
+    if y <= -big:
+        return 0xFF80
+    fy = float(y)
+    # candidates: the finite values around float(y) (float(y) is within an ulp of y)
+    idx = np.argsort(np.abs(_FIN_VALS - fy))[:6]
+    best, bestd = None, None
+    for i in idx:
+        v = Fraction(float(_FIN_VALS[i]))
+        d = abs(y - v)
+        b = int(_FIN[i])
+        if v == 0 and b == 0x8000:
+            continue
+        if best is None or d < bestd or (d == bestd and (b & 1) == 0 and (best & 1) == 1):
+            best, bestd = b, d
+    return best
+
+
+def _exact_rotation(bits):
+    """y = H x in exact rational arithmetic with scipy's Hadamard matrix."""
     from scipy.linalg import hadamard
-    H = hadamard(D).astype(np.float64)
+    D = bits.shape[-1]
+    H = hadamard(D)
+    x = [Fraction(float(v)) for v in codecs.bf16_to_f32(bits).astype(np.float64)]
+    return [sum((int(H[j, i]) * x[i] for i in range(D)), Fraction(0)) for j in range(D)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_matches_library_matrix_and_torch_rounding(D):
+    """Rows of multiples of 2^-6 below 4 in magnitude: every exact H x is then an
+    integer multiple of 2^-6 below 2^9, exact in float64 and in float32, so
+    scipy's Hadamard matrix in float64 gives it and torch's float32 -> bf16 cast
+    (round to nearest even) is the single rounding.  Many results are exact
+    ties at bf16's 8 significant bits."""
+    from scipy.linalg import hadamard
     rng = np.random.default_rng(11)
-    xi = rng.integers(-2, 3, size=(40, D)).astype(np.float32)        # exact in bf16 and in the sums
-    got = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(xi))).astype(np.float64)
-    assert np.array_equal(got, xi.astype(np.float64) @ H.T)
-    xr = codecs.bf16_to_f32(_bf16_bits(rng.standard_normal((200, D)) * 3.0))
-    ref = xr.astype(np.float64) @ H.T
-    got = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(xr))).astype(np.float64)
-    # bf16 rounding of the result (2^-9 relative) plus float32 sums (about 2^-24 * D * max|x|)
-    bound = np.abs(ref) * 2.0 ** -8 + 2.0 ** -20 * D * np.abs(xr).max(axis=-1, keepdims=True)
-    assert np.all(np.abs(got - ref) <= bound)
+    k = rng.integers(-255, 256, size=(400, D))
+    xr = (k * 2.0 ** -6).astype(np.float32)
+    bits = _bf16_bits(xr)
+    assert np.array_equal(codecs.bf16_to_f32(bits), xr)          # inputs exact in bf16
+    ref64 = xr.astype(np.float64) @ hadamard(D).T.astype(np.float64)
+    ref32 = ref64.astype(np.float32)
+    assert np.array_equal(ref32.astype(np.float64), ref64)       # exact in float32
+    want = torch.from_numpy(ref32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    want = np.where(ref32 == 0, np.uint16(0), want)              # an exact zero is +0
+    got = codecs.hadamard_rotate_bf16(bits)
+    assert np.array_equal(got, want)
+    # ties were exercised: results exactly halfway between two bf16 values
+    r = ref32.view(np.uint32)
+    assert ((r & 0xFFFF) == 0x8000).sum() > 100
+
+
+def test_hadamard_brute_force_on_wide_rows():
+    """Rows whose magnitudes span up to 2^120 (beyond any float64 evaluation,
+    through the arbitrary-precision path) and ordinary rows: each output equals
+    the nearest bf16 of the exact rational result, found by search."""
+    rng = np.random.default_rng(21)
+    D = 64
+    rows = []
+    for t in range(6):
+        x = rng.standard_normal(D).astype(np.float32)
+        if t % 2 == 0:
+            x *= np.float32(2.0) ** rng.integers(-60, 60, size=D).astype(np.float32)
+        rows.append(x)
+    bits = _bf16_bits(np.stack(rows))
+    got = codecs.hadamard_rotate_bf16(bits)
+    for r in range(bits.shape[0]):
+        want = [_nearest_bf16_brute(y) for y in _exact_rotation(bits[r])]
+        assert got[r].tolist() == want, r
+
+
+def test_hadamard_named_ties_subnormals_and_overflow():
+    """Two nonzero inputs a, b at positions 0 and 1 give outputs a + b (H[j][1] =
+    1) and a - b (H[j][1] = -1) in alternate positions."""
+    D = 64
+
+    def pair(a, b):
+        x = np.zeros(D, np.float32)
+        x[0], x[1] = a, b
+        bits = _bf16_bits(x)
+        assert codecs.bf16_to_f32(bits)[0] == np.float32(a) and codecs.bf16_to_f32(bits)[1] == np.float32(b)
+        y = codecs.hadamard_rotate_bf16(bits)
+        return int(y[0]), int(y[1])
+
+    one = 0x3F80
+    assert pair(1.0, 2.0 ** -8) == (one, 0x3F7F)                 # 1 + 2^-8: tie -> even 1.0; 1 - 2^-8 exact
+    assert pair(1.0 + 2.0 ** -7, 2.0 ** -8) == (0x3F82, 0x3F80)  # tie above an odd value rounds up; 1 exact
+    t = 2.0 ** -125 * (1 + 2.0 ** -7)                            # normal, last bit 2^-132
+    up, dn = pair(t, 2.0 ** -133)                                # +- half its last bit: both ties
+    assert up == 0x0102 and dn == 0x0100                        # odd last bit: ties to mantissas 2 and 0
+    assert pair(2.0 ** -130, 2.0 ** -133) == (0x0009, 0x0007)    # subnormal sums are exact
+    mx = float(codecs.bf16_to_f32(np.uint16(0x7F7F)))
+    # the last binade's ulp is 2^120: max + 2^119 is the tie with 2^128, which
+    # goes to the even pattern, the overflow; max - 2^119 ties to even 0x7F7E
+    assert pair(mx, 2.0 ** 120) == (0x7F80, 0x7F7E)
+    assert pair(mx, 2.0 ** 119) == (0x7F80, 0x7F7E)
+    assert pair(mx, 2.0 ** 118) == (0x7F7F, 0x7F7F)              # below halfway: stays finite
+    assert pair(-mx, -(2.0 ** 119)) == (0xFF80, 0xFF7E)
+    assert pair(0.0, 0.0) == (0x0000, 0x0000)
+    negz = np.full(D, 0x8000, np.uint16)                         # -0 everywhere: exact zeros are +0
+    assert (codecs.hadamard_rotate_bf16(negz) == 0).all()
+
+
+def test_hadamard_non_finite_rules():
+    from scipy.linalg import hadamard
+    D = 64
+    H = hadamard(D)
+    x = np.zeros(D, np.float32)
+    x[0] = np.inf
+    y = codecs.hadamard_rotate_bf16(_bf16_bits(x))
+    assert (y == 0x7F80).all()                                   # column 0 of H is all +1
+    x[1] = -np.inf                                               # +Inf and -Inf meet where H[j][1] = +1
+    y = codecs.hadamard_rotate_bf16(_bf16_bits(x))
+    assert np.array_equal(y, np.where(H[:, 1] > 0, 0x7FC0, 0x7F80).astype(np.uint16))
+    x[1] = 1.0
+    x[5] = np.nan
+    assert (codecs.hadamard_rotate_bf16(_bf16_bits(x)) == 0x7FC0).all()
 
 
 def test_hadamard_twice_is_D_times_identity_and_columns():
@@ -294,3 +411,55 @@ def test_hadamard_preserves_dot_products():
     hq = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(q))).astype(np.float64)
     hk = codecs.bf16_to_f32(codecs.hadamard_rotate_bf16(_bf16_bits(k))).astype(np.float64)
     assert np.array_equal((hq * hk).sum(-1), D * (q.astype(np.float64) * k).sum(-1))
+
+
+def test_hadamard_matrix_is_scipys():
+    from scipy.linalg import hadamard
+    for D in (2, 16, 64, 128):
+        assert np.array_equal(codecs.hadamard_matrix(D), hadamard(D))
+
+
+# ---- helpers that decide what the GPU comparison accepts ----
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_is_nan_code_matches_torch(fmt, tdt):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(tdt).to(torch.float32).isnan().numpy()
+    assert np.array_equal(codecs.fp8_is_nan_code(codes, fmt), ref)
+
+
+def test_f32_to_bf16_rne_matches_torch():
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(50000) * 10.0 ** rng.uniform(-40, 38, 50000)).astype(np.float32),
+        rng.integers(0, 2 ** 32, size=100000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ])
+    # exact ties: low half 0x8000 above an even and an odd bf16, both signs
+    hi = rng.integers(0, 0x7F7F, size=20000).astype(np.uint32)
+    ties = ((hi << 16) | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([3.4028235e38, -3.4028235e38, 3.3961e38, np.inf, -np.inf,
+                                                      0.0, -0.0, 1e-45, -1e-45])])
+    fin = ~np.isnan(x)
+    got = codecs.f32_to_bf16_rne(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[fin], want[fin])
+    assert (got[~fin] == 0x7FC0).all()
+    wt = torch.from_numpy(ties).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(codecs.f32_to_bf16_rne(ties), wt)
+    assert ((wt & 1) == 0).all()                                 # every tie went to an even pattern
+
+
+def test_int4_nan_elements_are_left_out():
+    """A NaN element does not enter the row's min / max and gets code 0; a row of
+    only NaNs keeps (NaN, NaN) and zero codes (the fmin / fmax rule of the
+    calibration)."""
+    x = np.array([[-1.0, np.nan, 2.0, 2.0], [np.nan] * 4, [0.5, np.nan, np.nan, 0.5]], np.float32)
+    codes, s, zp = codecs.int4_encode_rows(x)
+    c0, s0, z0 = codecs.int4_encode_rows(np.array([[-1.0, 2.0, 2.0]], np.float32))
+    assert s[0] == s0[0] and zp[0] == z0[0]
+    assert codes[0].tolist() == [c0[0][0], 0, c0[0][1], c0[0][2]]
+    assert np.isnan(s[1]) and np.isnan(zp[1]) and (codes[1] == 0).all()
+    # constant row guard: s = |min| = 0.5, zp = -1, both 0.5 entries at code 0 and exact
+    assert s[2] == np.float32(0.5) and zp[2] == -1.0 and codes[2].tolist() == [0, 0, 0, 0]
+    assert codecs.int4_decode(codes[2:3], s[2:3], zp[2:3])[0, 0] == np.float32(0.5)
