@@ -79,12 +79,15 @@ typedef enum kvq_dtype {
   KVQ_F32 = 5,
   /* Keys only: KVQ_INT4_ASYM codes of the Hadamard-rotated row (KVarN article,
    * technical context: a Hadamard rotation before asymmetric quantisation).  The
-   * rotation is the unnormalised Sylvester-Hadamard transform H x of the head_dim
-   * values, in float32 by the fast Walsh-Hadamard butterfly (stages h = 1, 2, ...,
-   * head_dim / 2, the pair at (i, i + h) becoming (a + b, a - b)), rounded to bf16.
-   * Decoding such a cache takes the query rotated by kvq_hadamard_rotate and
-   * softmax_scale / head_dim, since (H q) . (H k) = head_dim (q . k).  Values and
-   * metadata are laid out as KVQ_INT4_ASYM; V must be KVQ_INT4_ASYM. */
+   * rotation is the unnormalised Sylvester-Hadamard transform y = H x of the
+   * head_dim values, H[i][k] = (-1)^popcount(i & k), rounded once to bf16 (round
+   * to nearest even; an exact zero is +0): exact for rows whose magnitudes span
+   * less than 2^38, within one bf16 ulp otherwise.  The key such a slot holds is
+   * H y_hat / head_dim (H H = head_dim I).  Decode and verify take the query and
+   * softmax_scale exactly as for any other key format: the library rotates the
+   * query itself and folds the 1 / head_dim into the logit scale, since
+   * (H q) . y_hat = head_dim (q . H y_hat / head_dim).  Values and metadata are
+   * laid out as KVQ_INT4_ASYM; V must be KVQ_INT4_ASYM. */
   KVQ_INT4_HAD = 6
 } kvq_dtype;
 
@@ -141,7 +144,8 @@ kvq_status kvq_calibrate_scales(const uint16_t* x, int64_t num_tokens, int32_t n
  *          value (NaN -> a NaN code)
  *   INT4:  per row: s = (max - min) / 15, zp = RNE(-min / s) (s = |min| or 1 for
  *          a constant row), q = clamp(RNE(x / s) + zp, 0, 15); (s, zp) stored
- *          in the metadata
+ *          in the metadata.  NaN elements are left out of min and max and get
+ *          code 0; a row of only NaNs stores (NaN, NaN) and zero codes
  *   BF16:  copied
  * x / s is an IEEE-correctly-rounded float32 division.
  *   k_new, v_new  (device) bf16 [num_tokens][num_kv_heads][head_dim]
@@ -214,8 +218,8 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
  *   out_dtype     KVQ_BF16 (round to nearest even) or KVQ_F32
  *   out           (device) [batch][num_q_heads][head_dim] of out_dtype
  * Supported K/V dtype pairs: any of {INT8, FP8_E4M3, FP8_E5M2, BF16} for K and for
- * V independently, INT4 for both, and KVQ_INT4_HAD keys with INT4 values (q then
- * rotated by kvq_hadamard_rotate and softmax_scale divided by head_dim).
+ * V independently, INT4 for both, and KVQ_INT4_HAD keys with INT4 values (q and
+ * softmax_scale as for every format: the rotation of q is the library's).
  */
 kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -285,7 +289,9 @@ int64_t kvq_blocks_in_budget(uint64_t budget_bytes, int32_t k_dtype, int32_t v_d
 
 /*
  * kvq_hadamard_rotate — the KVQ_INT4_HAD rotation of bf16 rows (KVarN article,
- * technical context), for the query of a decode over rotated keys.
+ * technical context): the transform the cache write and conversion apply to
+ * rotated keys, for callers that rotate other rows the same way (decode and
+ * verify rotate their query themselves).
  *   x, out      (device) bf16 [num_rows][head_dim], 16-byte aligned; out may
  *               equal x (each row is read before it is written)
  *   num_rows    >= 0;  head_dim 64 or 128

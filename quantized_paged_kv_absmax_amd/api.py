@@ -8,6 +8,7 @@ and the current HIP stream.  Every step of the work runs in the HIP kernels.
     out = kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, scale)
 """
 
+import contextlib
 import ctypes
 
 import torch
@@ -33,6 +34,13 @@ def _ptr(t):
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Context for the binding's own allocations (output, workspace): made on the
+    stream the call enqueues on, so that torch's caching allocator orders their
+    reuse after that work and not after the current stream's."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _need(t, dtype, name, shape=None, device=None, min_numel=None):
@@ -167,18 +175,12 @@ def kvq_hadamard_rotate(x, out=None, stream=None):
     _need(x, torch.bfloat16, "x")
     D = x.shape[-1]
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     _need(out, torch.bfloat16, "out", shape=x.shape, device=x.device)
     st = _lib.load().kvq_hadamard_rotate(_ptr(x), x.numel() // max(D, 1), D, _ptr(out), _stream(stream))
     check(st, "kvq_hadamard_rotate")
     return out
-
-
-def _query_for(cache, q, softmax_scale, stream):
-    """Rotated-key caches take the rotated query and the logit scale / D (H H = D I)."""
-    if cache.k_dtype != _lib.INT4_HAD:
-        return q, softmax_scale
-    return kvq_hadamard_rotate(q, stream=stream), float(softmax_scale) / cache.head_dim
 
 
 def kvq_verify_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition=0):
@@ -209,18 +211,18 @@ def kvq_paged_attention_verify(cache, q, n_q, block_tables, seq_lens, max_seq_le
     _need(q, torch.bfloat16, "q", shape=(B * n_q, Hq, cache.head_dim), device=dev)
     T, D = B * n_q, cache.head_dim
     odt = _dt(out_dtype)
-    if out is None:
-        out = torch.empty((T, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+    need = kvq_verify_workspace_size(B, n_q, Hq, cache.num_kv_heads, D, max_seq_len, partition)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _need(out, _out_torch_dtype(odt), "out", shape=(T, Hq, D), device=dev)
     _opt(err_count, torch.int32, "err_count", dev)
-    need = kvq_verify_workspace_size(B, n_q, Hq, cache.num_kv_heads, D, max_seq_len, partition)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
-    q, softmax_scale = _query_for(cache, q, softmax_scale, stream)
     st = _lib.load().kvq_paged_attention_verify(
         ctypes.byref(s), _ptr(q), int(n_q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
         int(max_seq_len), Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out),
@@ -266,18 +268,18 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
     Hq, D = q.shape[1], cache.head_dim
     _need(q, torch.bfloat16, "q", shape=(B, Hq, D), device=dev)
     odt = _dt(out_dtype)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+    need = kvq_decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_seq_len, partition)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _need(out, _out_torch_dtype(odt), "out", shape=(B, Hq, D), device=dev)
     _opt(err_count, torch.int32, "err_count", dev)
-    need = kvq_decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_seq_len, partition)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = cache.struct() if struct is None else struct
-    q, softmax_scale = _query_for(cache, q, softmax_scale, stream)
     st = _lib.load().kvq_paged_attention_decode(
         ctypes.byref(s), _ptr(q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
         Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out), _ptr(err_count),

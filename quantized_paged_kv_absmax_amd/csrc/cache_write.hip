@@ -99,33 +99,53 @@ __device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, flo
   *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
 }
 
+// bf16 bits of a float64 value, rounded once to nearest even.  The value is
+// first narrowed to float32 toward zero with inexactness marked in the last bit
+// (round to odd): float32 keeps 16 bits beyond bf16's 8 at every magnitude,
+// subnormals included, so rounding that to nearest even gives the direct
+// rounding of the float64 value (a round-to-odd intermediate with at least two
+// extra bits makes the second rounding innocuous).  Past the bf16 range the
+// odd float32 maximum rounds on to infinity, as the direct rounding does.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+  const float f = __double2float_rz(v);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != v && v == v) u |= 1u;
+  return f32_to_bf16_bits(__uint_as_float(u));
+}
+
 // The unnormalised Walsh-Hadamard transform of a row held by LPR aligned lanes,
-// 8 values each (x[i] = element 8 j + i): stages h = 1, 2, 4 inside the lane,
+// 8 values each (x[i] = element 8 j + i): y = H x with H[i][k] =
+// (-1)^popcount(i & k), by the butterfly (stages h = 1, 2, 4 inside the lane,
 // then h = 8 .. D/2 between lanes j and j ^ (h / 8); the pair at (i, i + h)
-// becomes (a + b, a - b) in float32, stage by stage in increasing h, and the
-// result is rounded to bf16 (returned as float32).
+// becomes (a + b, a - b)) in float64, where every sum is exact while the row's
+// magnitudes span less than 2^38 (bf16 values carry 8 significant bits; D <=
+// 128 terms add 7 more), then rounded once to bf16 (returned as float32).  An
+// exact zero comes out as +0.
 template <int LPR>
 __device__ __forceinline__ void hadamard_row(float (&x)[8], int j) {
+  double y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (double)x[i];
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (!(i & h)) {
-        const float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
+        const double a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
       }
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) {
     const bool upper = j & m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float other = __shfl_xor(x[i], m, 64);
-      x[i] = upper ? other - x[i] : x[i] + other;
+      const double other = __shfl_xor(y[i], m, 64);
+      y[i] = upper ? other - y[i] : y[i] + other;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(f32_to_bf16_bits(x[i]));
+  for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(f64_to_bf16_rne(y[i] + 0.0));
 }
 
 // this lane's 16 source bytes of a row, and the row's scale

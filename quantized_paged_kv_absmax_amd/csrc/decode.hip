@@ -53,8 +53,7 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   const int groups = (prm.n_tiles + prm.wg_waves - 1) / prm.wg_waves;   // workgroups per (chunk, KV head)
   dim3 grid(a.n_chunks * groups, c.num_kv_heads);
   hipError_t e;
-  // rotated keys (DT_INT4H) are INT4 codes: the caller rotated the query alike
-  const int kt = (c.k_dtype == DT_INT4H) ? DT_INT4 : c.k_dtype;
+  const int kt = c.k_dtype;
   if (a.n_q > 1) e = launch_chunk_verify(prm, kt, c.v_dtype, c.head_dim, grid, s);
   else e = (c.head_dim == 128) ? launch_kv<128, false>(kt, c.v_dtype, prm, grid, s)
                                : launch_kv<64, false>(kt, c.v_dtype, prm, grid, s);

@@ -510,6 +510,66 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_rows_kernel(Params 
 }
 
 // ---------------------------------------------------------------------------
+// query rotation for rotated keys: y = H q, H[i][k] = (-1)^popcount(i & k) (the
+// rotation of the stored keys).  On the integer path lane group qg holds head-dim
+// positions qg * NL + local(s2, e), NL = 16 * D / 64, so the butterfly runs over
+// the local positions inside the lane, then over qg between lanes l and l ^ 16,
+// l and l ^ 32 (the pair at (i, i + h) becomes (a + b, a - b)), in float32.
+// ---------------------------------------------------------------------------
+
+template <int KT, int D>
+__host__ __device__ constexpr int q_local(int s2, int e) {
+  return q_dim<KT, D, true>(0, s2, e) - q_dim<KT, D, true>(0, 0, 0);
+}
+template <int KT, int D>
+constexpr bool q_lane_block_ok() {
+  constexpr int NL = 16 * (D / 64);
+  for (int qg = 0; qg < 4; ++qg)
+    for (int s2 = 0; s2 < D / 64; ++s2)
+      for (int e = 0; e < 16; ++e)
+        if (q_dim<KT, D, true>(qg, s2, e) != qg * NL + q_local<KT, D>(s2, e)) return false;
+  return true;
+}
+
+template <int KT, int D>
+__device__ __forceinline__ void rotate_query(float (&qv)[D / 64][16], int qg) {
+  constexpr int NSI = D / 64, NL = 16 * NSI;
+  static_assert(q_lane_block_ok<KT, D>(), "a lane group holds one contiguous block of head-dim positions");
+  float y[NL];
+#pragma unroll
+  for (int s2 = 0; s2 < NSI; ++s2)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) y[q_local<KT, D>(s2, e)] = qv[s2][e];
+#pragma unroll
+  for (int h = 1; h < NL; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (!(i & h)) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+  // v_permlane16_swap of a value with itself leaves the value of the even and
+  // of the odd 16-lane row of each pair; v_permlane32_swap that of each half
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[i]), __float_as_uint(y[i]), false, false);
+    const float other = __uint_as_float((qg & 1) ? r[0] : r[1]);
+    y[i] = (qg & 1) ? other - y[i] : y[i] + other;
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[i]), __float_as_uint(y[i]), false, false);
+    const float other = __uint_as_float((qg & 2) ? r[0] : r[1]);
+    y[i] = (qg & 2) ? other - y[i] : y[i] + other;
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < NSI; ++s2)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) qv[s2][e] = y[q_local<KT, D>(s2, e)];
+}
+
+// ---------------------------------------------------------------------------
 // the chunk kernel: one wave per (chunk, KV head)
 // ---------------------------------------------------------------------------
 
@@ -664,8 +724,12 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // read the round into registers, frees the stage, and the round after next is
 // issued into it before the round's arithmetic.  The page bytes are then read
 // once for all the tiles of a workgroup.
-template <int KT, int VT, int D, int CH, bool MQ>
+template <int KT_DECL, int VT, int D, int CH, bool MQ>
 __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
+  // rotated keys (DT_INT4H) are INT4 codes of H k: the same pages and products,
+  // with the query rotated alike when a segment's query rows are read
+  constexpr bool KROT = (KT_DECL == DT_INT4H);
+  constexpr int KT = KROT ? DT_INT4 : KT_DECL;
   static_assert(CH % 2 == 0, "pages are consumed in pairs by the PV product");
   static_assert(CH <= kNp, "pages per round fit the descriptor");
   using KG = Geo<KT, D>;
@@ -1086,11 +1150,17 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         const uint32_t wd = raw[s2][pos >> 3][(pos >> 1) & 3];
         return __uint_as_float((pos & 1) ? (wd & 0xffff0000u) : (wd << 16));
       };
+      float qv[NSI][16];
+#pragma unroll
+      for (int s2 = 0; s2 < NSI; ++s2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qv[s2][e] = qval(s2, e);
+      if constexpr (KROT) rotate_query<KT, D>(qv, qg);
       float amax = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < NSI; ++s2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(qval(s2, e)));
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(qv[s2][e]));
       amax = xor32_max(xor16_max(amax));
       const float sq = (amax > 0.0f) ? amax / 127.0f : 1.0f;
       const float inv = hv ? 1.0f / sq : 0.0f;
@@ -1107,7 +1177,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             // |x| <= 127 up to rounding, so the first digit lies in [-127, 127]
-            float x = qval(s2, 4 * i + k) * inv;
+            float x = qv[s2][4 * i + k] * inv;
 #pragma unroll
             for (int dg = 0; dg < 3; ++dg) {
               const float t = x + kM;
@@ -1134,7 +1204,8 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         qsum_i = (dsum[0] * 128.0f + dsum[1]) * 128.0f + dsum[2];
       }
       kq = hv ? kfac * sq * (1.0f / 16384.0f) : 0.0f;
-      kq4 = hv ? p.sm_log2 * sq * (1.0f / 16384.0f) : 0.0f;
+      // rotated keys: (H q) . (H k) = D (q . k), so the logit takes 1 / D more
+      kq4 = hv ? p.sm_log2 * sq * (1.0f / 16384.0f) * (KROT ? 1.0f / D : 1.0f) : 0.0f;
     } else {
       // step s: 8 bf16 values, one 16-byte read
       u32x4 raw[NS];
@@ -1612,9 +1683,10 @@ hipError_t launch_v(int vt, const Params& prm, dim3 grid, hipStream_t s) {
 
 template <int D, bool MQ>
 hipError_t launch_kv(int kt, int vt, const Params& prm, dim3 grid, hipStream_t s) {
-  if (kt == DT_INT4) {
+  if (kt == DT_INT4 || kt == DT_INT4H) {
     if (vt != DT_INT4) return hipErrorInvalidValue;
-    return launch_typed<DT_INT4, DT_INT4, D, MQ>(prm, grid, s);
+    return kt == DT_INT4 ? launch_typed<DT_INT4, DT_INT4, D, MQ>(prm, grid, s)
+                         : launch_typed<DT_INT4H, DT_INT4, D, MQ>(prm, grid, s);
   }
   switch (kt) {
     case DT_BF16: return launch_v<DT_BF16, D, MQ>(vt, prm, grid, s);

@@ -207,7 +207,15 @@ def assert_codes_equal(r, oracle_cache, inp, seqs=None):
         if dt in ("int4", "int4h"):
             gm = pick(getattr(r.cache, which + "_meta"), False).transpose(0, 2, 1, 3)[vm]
             em = pick(getattr(oracle_cache, which + "_meta"), True).transpose(0, 2, 1, 3)[vm]
-            assert np.array_equal(gm.view(np.uint32), em.view(np.uint32)), f"{which} int4 metadata differs"
+            assert meta_equal(gm, em), f"{which} int4 metadata differs"
+
+
+def meta_equal(got, ref):
+    """INT4 (scale, zero point) metadata: bit-equal float32 patterns, or NaN on
+    both sides (an all-NaN row's NaNs may differ in sign and payload)."""
+    g, e = np.asarray(got, np.float32), np.asarray(ref, np.float32)
+    both_nan = np.isnan(g) & np.isnan(e)
+    return bool(np.all((g.view(np.uint32) == e.view(np.uint32)) | both_nan))
 
 
 def bf16_half_ulp(x):
@@ -262,7 +270,7 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-__all__ = ["dev_bf16", "build_library_cache", "library_decode", "build_oracle_cache", "build_oracle_cache_sampled",
+__all__ = ["dev_bf16", "meta_equal", "build_library_cache", "library_decode", "build_oracle_cache", "build_oracle_cache_sampled",
            "query_rows",
            "seq_token_rows", "assert_codes_equal",
            "gate_errors", "oracle_decode", "sample_rows", "log", "softmax_scale", "math", "ceil_div"]

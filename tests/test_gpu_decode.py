@@ -249,3 +249,66 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(ValueError):
         kvq.kvq_calibrate_scales(x, "per_kv_head", "int8", torch.zeros(1, device=dev), torch.zeros(1, device=dev))
     torch.cuda.synchronize()
+
+
+def test_rotated_keys_through_the_c_abi_alone():
+    """KVQ_INT4_HAD keys, decode and two-token verify called straight through
+    ctypes with the caller's plain query and softmax scale: the library rotates
+    the query and folds 1 / head_dim in itself."""
+    import ctypes
+    from quantized_paged_kv_absmax_amd import _lib
+    from oracle import attention as oa
+    inp = make_decode_inputs(_workload("int4_had"), B=5, lens=("uniform", 30, 700))
+    w = inp.w
+    r = build_library_cache(w, inp)
+    o = build_oracle_cache(w, inp)
+    lib = _lib.load()
+    s = r.cache.struct()
+    sm = softmax_scale(w.D)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    B = w.B
+    for n_q in (1, 2):
+        inp2 = make_decode_inputs(w.with_(n_q=n_q))
+        assert np.array_equal(inp2.k_bits, inp.k_bits)
+        q = dev_bf16(inp2.q_bits)
+        out = torch.empty((B * n_q, w.Hq, w.D), dtype=torch.float32, device="cuda")
+        need = lib.kvq_verify_workspace_size(B, n_q, w.Hq, w.Hkv, w.D, inp.max_seq_len, 64)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+        args = (ctypes.byref(s), ctypes.c_void_p(q.data_ptr()))
+        tail = (ctypes.c_void_p(r.bt.data_ptr()), r.bt.shape[1], ctypes.c_void_p(r.sl.data_ptr()), B,
+                inp.max_seq_len, w.Hq, sm, 64, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _lib.F32,
+                ctypes.c_void_p(out.data_ptr()), None, stream)
+        if n_q == 1:
+            st = lib.kvq_paged_attention_decode(*args, *tail)
+            ref = oa.decode(o, inp2.q_bits, inp.block_tables, inp.seq_lens, sm)
+        else:
+            st = lib.kvq_paged_attention_verify(*args, n_q, *tail)
+            ref = oa.verify(o, inp2.q_bits, n_q, inp.block_tables, inp.seq_lens, sm)
+        assert st == _lib.OK
+        torch.cuda.synchronize()
+        mx, nbad = gate_errors(out, ref, "f32")
+        log(f"int4h through the C ABI, n_q={n_q}: max|err|={mx:.3e}")
+        assert nbad == 0
+
+
+def test_side_stream_call_keeps_its_own_temporaries():
+    """A decode enqueued on a non-current stream, with the workspace and output
+    allocated by the binding: those allocations belong to that stream, so
+    tensors allocated and filled on the current stream right after the call
+    cannot take their memory before the decode has run."""
+    inp, r, o, ref = _setup("llama8b_int8")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        out = kvq.kvq_paged_attention_decode(r.cache, r.q, r.bt, r.sl, inp.max_seq_len, softmax_scale(inp.w.D),
+                                             partition=64, out_dtype="f32", stream=side)
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(8)]   # on the current stream
+        outs.append(out)
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for out in outs:
+        mx, nbad = gate_errors(out, ref, "f32")
+        assert nbad == 0, mx

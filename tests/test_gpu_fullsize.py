@@ -25,8 +25,8 @@ from workloads import WORKLOADS, make_calibration_set, make_decode_inputs
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["llama8b_int8", "fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4",
-         "longctx_int8", "verify16_int8"]
+NAMES = ["llama8b_int8", "fp8_e4m3", "fp8_e4m3_s1", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16",
+         "int4", "int4_had", "longctx_int8", "verify16_int8"]
 N_SEQS = {"longctx_int8": 2}   # 32K-131K-token sequences: two suffice, four heads each
 N_HEADS = 4
 
