@@ -229,6 +229,33 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       void* out, int32_t* err_count, void* stream);
 
 /*
+ * kvq_paged_attention_decode_noalloc — kvq_paged_attention_decode without a
+ * caller-supplied workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing and calls no allocating routine.
+ *
+ * The split-KV partials go to a device array inside the library, one per GPU,
+ * of KVQ_DECODE_SCRATCH_BYTES, held from the library's first use on that GPU
+ * until the process ends.  Its device address is looked up on the first call on
+ * each device (the current device, which `stream` must belong to); that call is
+ * the only one that touches the HIP runtime beyond the launches.  The array
+ * needs no initial contents and keeps the last call's partials.  Calls that
+ * overlap in time on one GPU (other streams, other host threads) share it and
+ * race: serialise them.
+ * Arguments, results and errors as kvq_paged_attention_decode, plus
+ * KVQ_ERR_WORKSPACE when kvq_decode_workspace_size(...) of these sizes exceeds
+ * KVQ_DECODE_SCRATCH_BYTES, and KVQ_ERR_HIP when the array's address cannot be
+ * obtained.
+ */
+#define KVQ_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+kvq_status kvq_paged_attention_decode_noalloc(const kvq_cache* cache, const uint16_t* q,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                              int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                              int32_t out_dtype, void* out, int32_t* err_count, void* stream);
+
+/*
  * kvq_paged_attention_verify — several query tokens per sequence over the
  * cache, causally: speculative-decoding verification or a prefill chunk whose
  * K/V rows are already written.

@@ -18,12 +18,13 @@ PER_TENSOR, PER_KV_HEAD, PER_TOKEN_HEAD = range(3)
 
 DTYPES = {"bf16": BF16, "auto": BF16, "int8": INT8, "e4m3": FP8_E4M3, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
           "e5m2": FP8_E5M2, "fp8_e5m2": FP8_E5M2, "int4": INT4_ASYM, "f32": F32, "int4h": INT4_HAD}
+DECODE_SCRATCH_BYTES = 64 << 20   # KVQ_DECODE_SCRATCH_BYTES
 GRANULARITIES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD, "per_token_head": PER_TOKEN_HEAD}
 
 EXPORTS = ("kvq_calibrate_scales", "kvq_cache_write", "kvq_convert_cache", "kvq_decode_workspace_size",
            "kvq_paged_attention_decode", "kvq_paged_attention_verify", "kvq_verify_workspace_size",
            "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string", "kvq_abi_version",
-           "kvq_hadamard_rotate")
+           "kvq_hadamard_rotate", "kvq_paged_attention_decode_noalloc")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -61,6 +62,8 @@ def load():
     lib.kvq_decode_workspace_size.restype = SZ
     lib.kvq_paged_attention_decode.argtypes = [CP, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
     lib.kvq_paged_attention_decode.restype = I32
+    lib.kvq_paged_attention_decode_noalloc.argtypes = [CP, P, P, I32, P, I32, I32, I32, F, I32, I32, P, P, P]
+    lib.kvq_paged_attention_decode_noalloc.restype = I32
     lib.kvq_paged_attention_verify.argtypes = [CP, P, I32, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
     lib.kvq_paged_attention_verify.restype = I32
     lib.kvq_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]

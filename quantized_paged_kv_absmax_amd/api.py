@@ -286,3 +286,35 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
         _stream(stream))
     check(st, "kvq_paged_attention_decode")
     return out
+
+
+def kvq_paged_attention_decode_noalloc(cache, q, block_tables, seq_lens, max_seq_len, softmax_scale, partition=0,
+                                       out_dtype="bf16", out=None, err_count=None, stream=None, struct=None):
+    """kvq_paged_attention_decode with the library's own per-GPU scratch array as
+    workspace (no device allocation by the library).  Calls that overlap on one
+    GPU share that array: serialise them.  ``out`` is allocated here only when
+    not given."""
+    dev = cache.k_pages.device
+    _need(seq_lens, torch.int32, "seq_lens", device=dev)
+    if seq_lens.dim() != 1:
+        raise ValueError(f"seq_lens must be [B], got shape {tuple(seq_lens.shape)}")
+    B = seq_lens.shape[0]
+    _need(block_tables, torch.int32, "block_tables", device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_blocks], got shape {tuple(block_tables.shape)}")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][D], got shape {tuple(q.shape)}")
+    Hq, D = q.shape[1], cache.head_dim
+    _need(q, torch.bfloat16, "q", shape=(B, Hq, D), device=dev)
+    odt = _dt(out_dtype)
+    if out is None:
+        with _on(stream):
+            out = torch.empty((B, Hq, D), dtype=_out_torch_dtype(odt), device=dev)
+    _need(out, _out_torch_dtype(odt), "out", shape=(B, Hq, D), device=dev)
+    _opt(err_count, torch.int32, "err_count", dev)
+    s = cache.struct() if struct is None else struct
+    st = _lib.load().kvq_paged_attention_decode_noalloc(
+        ctypes.byref(s), _ptr(q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
+        Hq, float(softmax_scale), int(partition), odt, _ptr(out), _ptr(err_count), _stream(stream))
+    check(st, "kvq_paged_attention_decode_noalloc")
+    return out

@@ -7,7 +7,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kvq_launch.h"
+
+// Decode workspace for kvq_paged_attention_decode_noalloc: one array per GPU,
+// zero at load and held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address reaches kernels.
+static __device__ __align__(256) uint8_t scratch[KVQ_DECODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -197,12 +205,37 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                     out, err_count, stream);
 }
 
-kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q, int32_t n_q,
-                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                      int32_t num_q_heads, float softmax_scale, int32_t partition, void* workspace,
-                                      size_t workspace_bytes, int32_t out_dtype, void* out, int32_t* err_count,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// the device address of this GPU's `scratch` array, looked up on the first call
+// on each device (with that device current) and kept
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kvq_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KVQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
+// decode / verify; with use_scratch the workspace is this GPU's scratch array
+// (workspace and workspace_bytes are then ignored)
+kvq_status attention_impl(const kvq_cache* cache, const uint16_t* q, int32_t n_q, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                          int32_t num_q_heads, float softmax_scale, int32_t partition, void* workspace,
+                          size_t workspace_bytes, int32_t out_dtype, void* out, int32_t* err_count, void* stream,
+                          bool use_scratch) {
   const kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (!kvq::decode_supported(cache->k_dtype, cache->v_dtype, cache->head_dim)) return KVQ_ERR_UNSUPPORTED;
@@ -239,6 +272,12 @@ kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q,
   a.ws_rec = nullptr;
   if (sp.n_chunks > 1) {
     const WsLayout lay = workspace_layout(batch, (int64_t)n_q * num_q_heads, cache->head_dim, sp.n_chunks);
+    if (use_scratch) {
+      if ((size_t)lay.total > (size_t)KVQ_DECODE_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+      const kvq_status ss = scratch_of_current_device(&workspace);
+      if (ss != KVQ_OK) return ss;
+      workspace_bytes = KVQ_DECODE_SCRATCH_BYTES;
+    }
     if (!workspace) return KVQ_ERR_WORKSPACE;
     if (workspace_bytes < (size_t)lay.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
@@ -252,6 +291,30 @@ kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q,
   a.out = out;
   a.err = err_count;
   return from_hip(kvq::launch_decode(view(cache), a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q, int32_t n_q,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      int32_t num_q_heads, float softmax_scale, int32_t partition, void* workspace,
+                                      size_t workspace_bytes, int32_t out_dtype, void* out, int32_t* err_count,
+                                      void* stream) {
+  return attention_impl(cache, q, n_q, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
+                        softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream,
+                        false);
+}
+
+kvq_status kvq_paged_attention_decode_noalloc(const kvq_cache* cache, const uint16_t* q,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                              int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                              int32_t out_dtype, void* out, int32_t* err_count, void* stream) {
+  return attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
+                        softmax_scale, partition, nullptr, 0, out_dtype, out, err_count, stream, true);
 }
 
 kvq_status kvq_hadamard_rotate(const uint16_t* x, int64_t num_rows, int32_t head_dim, uint16_t* out,
