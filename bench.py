@@ -49,11 +49,13 @@ def parse():
     ap.add_argument("--counter-summary", nargs=4, metavar=("CSV_A", "CSV_B", "OUT", "COMMAND"),
                     help="write per-page instruction and wait counters of the chunk kernels (headline decode "
                          "and 16-token verify) from two rocprofv3 --pmc runs")
-    ap.add_argument("--traffic-summary", nargs=7,
-                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES", "OUT",
-                             "COMMAND"),
-                    help="write HBM bytes per decode call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs "
-                         "of the decode and of the copy probe, and exit")
+    ap.add_argument("--traffic-summary", nargs=8,
+                    metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_BYTES",
+                             "OUT", "COMMAND"),
+                    help="write HBM bytes per decode call of WORKLOAD from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "runs of --profile-workload WORKLOAD and of the copy probe, and exit")
+    ap.add_argument("--profile-workload", default=None, metavar="NAME",
+                    help="only build workload NAME and run its decode calls (for rocprofv3 runs of one workload)")
     return ap.parse_args()
 
 
@@ -114,7 +116,7 @@ def counter_summary(csv_a, csv_b, out, command):
     print("\n".join(lines))
 
 
-def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out, command):
+def traffic_summary(workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out, command):
     """HBM bytes per decode call (chunk + reduce kernels) from FETCH_SIZE / WRITE_SIZE,
     each scaled by what the same counter reads for a copy of known size."""
     import csv
@@ -142,11 +144,13 @@ def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, ou
     f_scale, w_scale = copy_bytes / cf, copy_bytes / cw
     fetch, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     cf_chunk, n = avg(fetch, "decode_chunk_kernel")
-    cf_red, _ = avg(fetch, "decode_reduce_kernel")
+    cf_red, _ = avg(fetch, "decode_reduce")
     cw_chunk, _ = avg(wr, "decode_chunk_kernel")
-    cw_red, _ = avg(wr, "decode_reduce_kernel")
+    cw_red, _ = avg(wr, "decode_reduce")
     total = (cf_chunk + cf_red) * f_scale + (cw_chunk + cw_red) * w_scale
-    lines = ["rocprofv3 HBM traffic of one kvq_paged_attention_decode call (llama8b_int8 workload)", "",
+    from workloads import WORKLOADS, make_decode_inputs
+    alg = kv_bytes(make_decode_inputs(WORKLOADS[workload]))
+    lines = [f"rocprofv3 HBM traffic of one kvq_paged_attention_decode call ({workload} workload)", "",
              "command:", "  " + command, "",
              f"kernel_source_hash: {decode_source_hash()}",
              f"copy_probe_bytes: {copy_bytes:.0f}",
@@ -157,6 +161,8 @@ def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, ou
              f"decode_chunk_kernel write_bytes (scaled): {cw_chunk * w_scale:.0f}",
              f"decode_reduce_kernel fetch_bytes (scaled): {cf_red * f_scale:.0f}",
              f"decode_reduce_kernel write_bytes (scaled): {cw_red * w_scale:.0f}",
+             f"algorithmic_kv_bytes: {alg}",
+             f"traffic_over_algorithmic: {total / alg:.4f}",
              f"hbm_bytes_per_launch: {total:.0f}"]
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -348,42 +354,84 @@ class GpuWorkload:
         return {"tokens": int(x.shape[0]), "us": t * 1e6, "gbs": x.numel() * 2 / t / 1e9}
 
 
-def time_steps(gw, steps, warmup, with_write=True, event_every=1):
-    """Warmup, then K timed steps bracketed by synchronize.  HIP events around
-    the decode launch of every event_every-th step give the decode call's own
-    average duration; an event pair between two launches costs the step several
-    microseconds (the launches can no longer overlap), so the headline step
-    samples them instead of bracketing every decode."""
+def time_steps(gw, steps, warmup, with_write=True):
+    """Warmup, then K timed steps (write + decode) bracketed by synchronize and
+    one event pair; returns ms per step."""
     torch = gw.torch
     for i in range(warmup):
         if with_write:
             gw.write_new(i)
         gw.decode(i)
     torch.cuda.synchronize()
-    sampled = [i for i in range(steps) if i % event_every == 0]
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for i in range(steps):
         if with_write:
             gw.write_new(i)
-        e = ev.get(i)
-        if e is not None:
-            e[0].record()
         gw.decode(i)
-        if e is not None:
-            e[1].record()
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    dec = np.array([a.elapsed_time(b) for a, b in ev.values()])
-    return total_ms / steps, dec
+    return start.elapsed_time(end) / steps
 
 
-def cpu_baseline(min_s=10.0):
-    """The oracle's decode on host cores over a bounded sample of the headline workload:
-    whole passes over its sequences, one sequence at a time, until min_s of CPU time."""
+def time_decode_calls(gw, samples=60, batch=10, warmup=5):
+    """The decode call alone, on the stream the library launches on (torch's
+    current stream): ``samples`` event pairs, each around ``batch`` calls launched
+    back to back (rotating pool copies), so that the per-call figure holds the
+    kernels and the gaps between them but not an event's own launch latency.
+    Also ``samples`` single calls each between its own event pair (that latency
+    included).  Returns per-call microseconds: (batched samples, single samples)."""
+    torch = gw.torch
+    for i in range(warmup):
+        gw.decode(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    k = 0
+    for a, b in ev:
+        a.record()
+        for _ in range(batch):
+            gw.decode(k)
+            k += 1
+        b.record()
+    torch.cuda.synchronize()
+    batched = np.array([a.elapsed_time(b) * 1e3 / batch for a, b in ev])
+    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for a, b in ev1:
+        a.record()
+        gw.decode(k)
+        k += 1
+        b.record()
+    torch.cuda.synchronize()
+    single = np.array([a.elapsed_time(b) * 1e3 for a, b in ev1])
+    return batched, single
+
+
+def call_stats(gw, batched, single, traffic=None):
+    med = float(np.median(batched))
+    gbs = gw.kv_bytes / (med * 1e-6) / 1e9
+    d = {"decode_us": med, "decode_us_p10_p90": [float(np.percentile(batched, 10)), float(np.percentile(batched, 90))],
+         "decode_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "kv_mb": gw.kv_bytes / 1e6,
+         "single_call_us": float(np.median(single)), "samples": f"{len(batched)} x 10 calls"}
+    if traffic is not None:
+        d["traffic_bytes"] = traffic
+        d["traffic_over_algorithmic"] = traffic / gw.kv_bytes
+    return d
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(min_s=8.0):
+    """The oracle's decode on host cores over a bounded sample of the headline
+    workload: whole passes over its sequences, one sequence at a time, until min_s
+    of wall time, first with every BLAS thread the host gives, then with one."""
     import threadpoolctl
     from oracle import attention as oa
     from oracle import cache as oc
@@ -397,20 +445,48 @@ def cpu_baseline(min_s=10.0):
     cache = oc.PagedCache(inp.num_blocks, w.Hkv, w.D, "int8", "int8", k_scale=ks, v_scale=vs)
     cache.write(inp.k_bits, inp.v_bits, inp.slot_mapping)
     sm = float(np.float32(1.0) / np.sqrt(np.float32(w.D)))
+
+    def run():
+        done, nbytes = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min_s:
+            b = done % w.B
+            oa.decode(cache, inp.q_bits, inp.block_tables, inp.seq_lens, sm, seqs=[b])
+            nbytes += int(inp.seq_lens[b]) * w.Hkv * 2 * w.D
+            done += 1
+        return done, nbytes, time.perf_counter() - t0
+
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    done, nbytes = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < min_s:
-        b = done % w.B
-        oa.decode(cache, inp.q_bits, inp.block_tables, inp.seq_lens, sm, seqs=[b])
-        nbytes += int(inp.seq_lens[b]) * w.Hkv * 2 * w.D
-        done += 1
-    dt = time.perf_counter() - t0
+    done, nbytes, dt = run()
+    with threadpoolctl.threadpool_limits(1):
+        done1, nbytes1, dt1 = run()
+    try:
+        affinity = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = []
+    aff = f"{len(affinity)} cpus ({affinity[0]}-{affinity[-1]})" if affinity else "unknown"
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "one_thread_gbs": nbytes1 / dt1 / 1e9,
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "affinity": aff,
             "sample": f"oracle fp64 decode, one sequence at a time, of {done} sequence decodes "
                       f"({done / w.B:.2f} passes over the {w.B} sequences of the llama8b_int8 workload; "
-                      f"{nbytes / 1e6:.1f} MB of int8 KV in {dt:.1f} s); host os.cpu_count()={os.cpu_count()}"}
+                      f"{nbytes / 1e6:.1f} MB of int8 KV in {dt:.1f} s) with {threads} BLAS threads, then "
+                      f"{done1} sequence decodes ({nbytes1 / 1e6:.1f} MB in {dt1:.1f} s) with one thread"}
+
+
+def profile_workload(name):
+    """One workload's decode calls alone (no headline), for a rocprofv3 run whose
+    per-kernel figures then belong to that workload only."""
+    import torch
+    import quantized_paged_kv_absmax_amd as kvq
+    kvq.load()
+    torch.cuda.set_device(0)
+    gw = GpuWorkload(name, "cuda:0")
+    batched, single = time_decode_calls(gw, samples=10)
+    d = call_stats(gw, batched, single)
+    print(json.dumps({"profile_workload": name, "decode_us": d["decode_us"], "decode_gbs": d["decode_gbs"],
+                      "kv_bytes": gw.kv_bytes, "calls": 10 * 10 + 10 + 5}))
 
 
 def main():
@@ -431,6 +507,9 @@ def main():
     if args.counter_summary:
         counter_summary(*args.counter_summary)
         return
+    if args.profile_workload:
+        profile_workload(args.profile_workload)
+        return
     import torch
     import quantized_paged_kv_absmax_amd as kvq
     kvq.load()
@@ -440,40 +519,34 @@ def main():
     gw = GpuWorkload("llama8b_int8", device)
     print(f"[bench] llama8b_int8 ready: {gw.inp.seq_lens.sum()} tokens, KV {gw.kv_bytes / 1e6:.1f} MB, "
           f"R={gw.R} rotating copies (gen {gw.gen_s:.1f}s)", file=sys.stderr, flush=True)
-    ms_step, dec = time_steps(gw, args.steps, args.warmup, with_write=True, event_every=8)
-    dec_ms = float(dec.mean())
+    ms_step = time_steps(gw, args.steps, args.warmup, with_write=True)
     value = gw.kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = gw.kv_bytes / (dec_ms * 1e-3) / 1e9
     khash = decode_source_hash()
     traffic = read_traffic("llama8b_int8", khash)
+    batched, single = time_decode_calls(gw)
+    head = call_stats(gw, batched, single, traffic)
+    achieved = head["decode_gbs"]
     # write alone: the 1-token-per-sequence cache write of the step
     wt = gw._events(lambda: gw.write_new(0), 50)
-    per_dtype = {"int8 (llama8b_int8)": {"decode_us": dec_ms * 1e3, "decode_gbs": achieved,
-                                         "frac_hbm": achieved / HBM_PEAK_GBS,
-                                         "decode_us_p10_p90": [float(np.percentile(dec, 10) * 1e3),
-                                                               float(np.percentile(dec, 90) * 1e3)]}}
+    per_dtype = {"int8 (llama8b_int8)": head}
     extras = {"llama8b_int8": dict(gw.extra, step_write_us=wt * 1e6)}
     del gw
     torch.cuda.empty_cache()
 
     if not args.quick:
-        names = ["fp8_e4m3", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4", "int4_had", "longctx_int8",
-                 "verify16_int8"]
+        names = ["fp8_e4m3", "fp8_e4m3_s1", "fp8_e5m2", "fp8_hybrid", "fp8_e4m3_head", "fp8_e5m2_cal", "bf16", "int4",
+                 "int4_had", "longctx_int8", "verify16_int8"]
         if args.only:
             names = [n for n in args.only.split(",") if n]
         for name in names:
             g2 = GpuWorkload(name, device)
-            steps = max(20, args.steps // (4 if name == "longctx_int8" else 1))
-            ms_call, d2 = time_steps(g2, steps, 5, with_write=False, event_every=4)
-            t = float(d2.mean())
-            gbs = g2.kv_bytes / (t * 1e-3) / 1e9
-            # decode_us: one call bracketed by events; back_to_back_us: the time per
-            # call over the whole run, calls launched back to back
-            per_dtype[f"{g2.w.k_dtype}/{g2.w.v_dtype} ({name})"] = {
-                "decode_us": t * 1e3, "decode_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "kv_mb": g2.kv_bytes / 1e6,
-                "back_to_back_us": ms_call * 1e3}
+            samples = 20 if name == "longctx_int8" else 40
+            b2, s2 = time_decode_calls(g2, samples=samples)
+            d = call_stats(g2, b2, s2, read_traffic(name, khash))
+            per_dtype[f"{g2.w.k_dtype}/{g2.w.v_dtype} ({name})"] = d
             extras[name] = g2.extra
-            print(f"[bench] {name}: decode {t * 1e3:.1f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+            print(f"[bench] {name}: decode {d['decode_us']:.1f} us, {d['decode_gbs']:.0f} GB/s", file=sys.stderr,
+                  flush=True)
             del g2
             torch.cuda.empty_cache()
 
@@ -501,7 +574,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "kvq_paged_attention_decode call: decode_chunk_kernel<INT8,INT8,128> + "
-                               "decode_reduce_kernel<128>", "kernel_source_hash": khash},
+                               "decode_reduce_kernel<128>",
+                     "timing": "median over 60 event pairs, each around 10 back-to-back calls on the launch "
+                               "stream (p10/p90 in per_dtype)",
+                     "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "per_dtype": per_dtype,
         "extra": extras,

@@ -187,38 +187,53 @@ __device__ __forceinline__ void store_row(const RowSide& sd, const RowIn& in, in
                        sd.meta ? sd.meta + dst_row_idx * 2 : nullptr, j);
 }
 
+// Each lane takes kRowsPerLane rows (kRowsPerLane x 16 bytes in flight before any
+// encode); the rows of one pass are consecutive, the passes of a workgroup too.
+constexpr int kRowsPerLane = 4;
+
 // R32: the row count fits 31 bits, so (token, head) come from a 32-bit division
 template <int D, bool R32>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSide v, const int64_t* slots,
                                                                int64_t T, int Hkv, int64_t num_slots,
                                                                int32_t* err) {
   constexpr int LPR = D / 8;
-  constexpr int RPB = kThreads / LPR;  // rows per block
+  constexpr int RPB = kThreads / LPR;  // rows per pass
   const RowSide& sd = (blockIdx.y == 0) ? k : v;
   const int j = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  if (row >= T * Hkv) return;
-  int64_t t;
-  int h;
-  if constexpr (R32) {
-    t = (int64_t)((uint32_t)row / (uint32_t)Hkv);
-    h = (int)((uint32_t)row - (uint32_t)t * (uint32_t)Hkv);
-  } else {
-    t = row / Hkv;
-    h = (int)(row % Hkv);
+  const int64_t rows = T * Hkv;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB * kRowsPerLane + threadIdx.x / LPR;
+  // every row's source, scale and slot loads go out before the first store
+  RowIn in[kRowsPerLane];
+  int64_t slot[kRowsPerLane];
+  int hh[kRowsPerLane];
+#pragma unroll
+  for (int u = 0; u < kRowsPerLane; ++u) {
+    const int64_t row = row0 + (int64_t)u * RPB;
+    const int64_t rr = row < rows ? row : rows - 1;
+    int64_t t;
+    int h;
+    if constexpr (R32) {
+      t = (int64_t)((uint32_t)rr / (uint32_t)Hkv);
+      h = (int)((uint32_t)rr - (uint32_t)t * (uint32_t)Hkv);
+    } else {
+      t = rr / Hkv;
+      h = (int)(rr % Hkv);
+    }
+    in[u] = load_row<D>(sd, sd.src + rr * D, h, j);
+    slot[u] = row < rows ? slots[t] : -1;
+    hh[u] = h;
   }
-  // the row's loads go out together with the slot's: one memory round trip
-  // before the store, not two
-  const RowIn in = load_row<D>(sd, sd.src + row * D, h, j);
-  const int64_t slot = slots[t];
-  if (slot < 0) return;
-  if (slot >= num_slots) {
-    if (err && blockIdx.y == 0 && h == 0 && j == 0) atomicAdd(err, 1);
-    return;
+#pragma unroll
+  for (int u = 0; u < kRowsPerLane; ++u) {
+    const int64_t sl = slot[u];
+    if (sl < 0) continue;                       // uniform over the row's lanes
+    if (sl >= num_slots) {
+      if (err && blockIdx.y == 0 && hh[u] == 0 && j == 0) atomicAdd(err, 1);
+      continue;
+    }
+    const int64_t blk = sl / 16, off = sl % 16;
+    store_row<D>(sd, in[u], (blk * Hkv + hh[u]) * 16 + off, j);
   }
-  const int64_t blk = slot / 16, off = slot % 16;
-  const int64_t dst = (blk * Hkv + h) * 16 + off;
-  store_row<D>(sd, in, dst, j);
 }
 
 template <int D>
@@ -228,11 +243,21 @@ __global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v,
   constexpr int RPB = kThreads / LPR;
   const RowSide& sd = (blockIdx.y == 0) ? k : v;
   const int j = threadIdx.x % LPR;
-  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // row within the block range
-  if (r >= (int64_t)n_blocks * Hkv * 16) return;
-  const int64_t dst = (int64_t)first_block * Hkv * 16 + r;          // same slot in source and dest
-  const int h = (int)((dst / 16) % Hkv);
-  store_row<D>(sd, load_row<D>(sd, sd.src + dst * D, h, j), dst, j);
+  const int64_t rows = (int64_t)n_blocks * Hkv * 16;                 // rows of the block range
+  const int64_t r0 = (int64_t)blockIdx.x * RPB * kRowsPerLane + threadIdx.x / LPR;
+  RowIn in[kRowsPerLane];
+#pragma unroll
+  for (int u = 0; u < kRowsPerLane; ++u) {
+    const int64_t r = min(r0 + (int64_t)u * RPB, rows - 1);
+    const int64_t dst = (int64_t)first_block * Hkv * 16 + r;        // same slot in source and dest
+    in[u] = load_row<D>(sd, sd.src + dst * D, (int)((dst / 16) % Hkv), j);
+  }
+#pragma unroll
+  for (int u = 0; u < kRowsPerLane; ++u) {
+    const int64_t r = r0 + (int64_t)u * RPB;
+    if (r >= rows) break;                       // uniform over the row's lanes
+    store_row<D>(sd, in[u], (int64_t)first_block * Hkv * 16 + r, j);
+  }
 }
 
 template <int D>
@@ -279,7 +304,8 @@ hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const u
   const int64_t num_slots = (int64_t)c.num_blocks * 16;
   const bool r32 = rows <= 0x7fffffff;
   if (c.head_dim == 128) {
-    dim3 grid((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)), 2);
+    constexpr int per = kThreads / 16 * kRowsPerLane;
+    dim3 grid((unsigned)((rows + per - 1) / per), 2);
     if (r32)
       hipLaunchKernelGGL((cache_write_kernel<128, true>), grid, dim3(kThreads), 0, s, k, v, slots, T,
                          c.num_kv_heads, num_slots, err);
@@ -287,7 +313,8 @@ hipError_t launch_cache_write(const CacheView& c, const uint16_t* k_new, const u
       hipLaunchKernelGGL((cache_write_kernel<128, false>), grid, dim3(kThreads), 0, s, k, v, slots, T,
                          c.num_kv_heads, num_slots, err);
   } else {
-    dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)), 2);
+    constexpr int per = kThreads / 8 * kRowsPerLane;
+    dim3 grid((unsigned)((rows + per - 1) / per), 2);
     if (r32)
       hipLaunchKernelGGL((cache_write_kernel<64, true>), grid, dim3(kThreads), 0, s, k, v, slots, T,
                          c.num_kv_heads, num_slots, err);
@@ -313,11 +340,13 @@ hipError_t launch_convert(const CacheView& c, const uint16_t* k_src, const uint1
   const RowSide k = side(c, true, k_src), v = side(c, false, v_src);
   const int64_t rows = (int64_t)n_blocks * c.num_kv_heads * 16;
   if (c.head_dim == 128) {
-    dim3 grid((unsigned)((rows + kThreads / 16 - 1) / (kThreads / 16)), 2);
+    constexpr int per = kThreads / 16 * kRowsPerLane;
+    dim3 grid((unsigned)((rows + per - 1) / per), 2);
     hipLaunchKernelGGL(convert_kernel<128>, grid, dim3(kThreads), 0, s, k, v, first_block, n_blocks,
                        c.num_kv_heads);
   } else {
-    dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)), 2);
+    constexpr int per = kThreads / 8 * kRowsPerLane;
+    dim3 grid((unsigned)((rows + per - 1) / per), 2);
     hipLaunchKernelGGL(convert_kernel<64>, grid, dim3(kThreads), 0, s, k, v, first_block, n_blocks,
                        c.num_kv_heads);
   }

@@ -704,13 +704,16 @@ constexpr int kTail = 1 << 5;    // holds the sequence's last page (tokens past 
 constexpr int kWhole = 1 << 6;   // the segment is the whole sequence
 constexpr int kQBuf = 1 << 7;    // query buffer of the segment (segments alternate)
 
+// inclusive prefix sum over the wave by DPP moves: shifts by 1, 2, 4, 8 inside
+// each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
+// added to rows 1 and 3 and lane 31 to rows 2 and 3 (row broadcasts)
 __device__ __forceinline__ int wave_incl_sum(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -794,17 +797,23 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   const int cap = min(p.max_seq_len, p.max_blocks_per_seq * 16);
   const bool counter = (tau == 0 && w == 0 && kvh == 0);   // the one wave that counts clamped lengths
 
-  // warm the caches with the block table: each wave pulls one 256-byte slice of
-  // it (into a ring stage not in use yet), so that the scalar loads of block ids
-  // after the length scan find their lines in L2 or the Infinity Cache.  Not with
-  // a shared ring: another wave's stage-1 DMA could land before this one.
+  // warm the caches with the block table (into a ring stage not in use yet; its
+  // later DMAs are younger and land after these), so that the scalar loads of
+  // block ids after the length scan hit in L2.  Workgroups go to the XCDs in turn
+  // (linear id modulo 8), and each XCD has its own L2: the waves of one XCD,
+  // those with equal id modulo 8, pull one copy of the table between them, up to
+  // 4 KB per wave.  Not with a shared ring: another wave's stage-1 DMA could land
+  // before this one.
   if constexpr (!MQ) {
     const size_t bt_bytes = (size_t)B * p.max_blocks_per_seq * 4;
-    const size_t off = ((size_t)kvh * gridDim.x + blockIdx.x) * 256;
+    const size_t wid = (size_t)kvh * gridDim.x + blockIdx.x;
+    const size_t per_xcd = ((size_t)gridDim.x * gridDim.y + 7) / 8;
+    const size_t kb = min((bt_bytes + per_xcd * 1024 - 1) / (per_xcd * 1024), (size_t)4);   // KB per wave
+    const size_t off = (wid / 8) * kb * 1024;
     if (off < bt_bytes) {
       const auto rb = page_rsrc(reinterpret_cast<const uint8_t*>(p.block_tables) + off,
-                                (int)min(bt_bytes - off, (size_t)256));
-      dma4(rb, lds1, 4 * lane);
+                                (int)min(bt_bytes - off, kb * 1024));
+      for (int t = 0; t < (int)kb; ++t) dma16(rb, lds1 + 1024 * t, 1024 * t + 16 * lane);
     }
   }
 
@@ -1598,10 +1607,11 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   Desc<CH> da = next();
   if constexpr (!kEarly) {
     if (da.info & kNp) {
+      // the first round's DMA goes out before the second round's block ids are read
+      issue(da, S0{});
       Desc<CH> dn = next();
       Desc<CH> db;
       auto none = []() __attribute__((always_inline)) {};
-      issue(da, S0{});
       while (true) {
         if (dn.info & kNp) issue(dn, S1{});
         db = dn;

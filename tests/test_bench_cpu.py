@@ -34,7 +34,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     chunk = "void kvq::(anonymous namespace)::decode_chunk_kernel<1, 1, 128, 2, false>(kvq::Params)"
-    red = "void kvq::(anonymous namespace)::decode_reduce_kernel<128>(kvq::Params)"
+    red = "void kvq::(anonymous namespace)::decode_reduce_rows_kernel<128>(kvq::Params)"
     copy = "__amd_rocclr_copyBuffer"
     # FETCH_SIZE reads half the bytes moved, WRITE_SIZE all of them (in KiB), on the copy of 1 MiB
     _csv(tmp_path / "cf.csv", [[1, copy, "FETCH_SIZE", 512.0], [2, copy, "FETCH_SIZE", 512.0]])
@@ -44,7 +44,7 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
                               [7, red, "FETCH_SIZE", 10.0]])
     _csv(tmp_path / "w.csv", [[5, chunk, "WRITE_SIZE", 4.0], [7, red, "WRITE_SIZE", 2.0]])
     out = tmp_path / "traffic.txt"
-    bench.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+    bench.traffic_summary("tiny_int8", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
                           str(tmp_path / "cw.csv"), str(1 << 20), str(out), "cmd")
     vals = dict(l.split(": ", 1) for l in out.read_text().splitlines() if ": " in l)
     assert float(vals["fetch_scale (copy bytes / copy FETCH_SIZE bytes)"]) == pytest.approx(2.0)
@@ -52,6 +52,10 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     # per call: (mean chunk 200 + reduce 10) KiB x 2 fetched, (4 + 2) KiB written
     assert float(vals["hbm_bytes_per_launch"]) == pytest.approx((210 * 2 + 6) * 1024)
     assert vals["kernel_source_hash"] == bench.decode_source_hash()
+    # tiny_int8: sequences of 17 and 33 tokens, 4 KV heads, 2 x 64 bytes per token-head
+    assert int(vals["algorithmic_kv_bytes"]) == (17 + 33) * 4 * 128
+    assert float(vals["traffic_over_algorithmic"]) == pytest.approx((210 * 2 + 6) * 1024 / ((17 + 33) * 4 * 128),
+                                                                     rel=1e-4)
 
 
 def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
