@@ -226,7 +226,9 @@ def int4_row_params(x):
         s  = fl32(fl32(mx - mn) / 15)
         if s == 0 or s is not finite:  s = |mn| if mn != 0 else 1.0
         zp = RNE(fl32(-mn / s))                 (an integer held in float32,
-                                                 not clamped)
+                                                 not clamped; +0 when zero, since
+                                                 a row holding -0 and +0 has
+                                                 either as its minimum)
     NaN elements are left out of min and max (fmin / fmax, as the calibration
     does); a row of only NaNs gets (NaN, NaN).
     Returns (s, zp), float32 arrays over the leading axes.
@@ -241,7 +243,7 @@ def int4_row_params(x):
     bad = (s == 0) | ~np.isfinite(s)
     guard = np.where(mn != 0, np.abs(mn), F32(1.0)).astype(F32)
     s = np.where(bad, guard, s).astype(F32)
-    zp = np.rint(_div32(-mn, s)).astype(F32)
+    zp = (np.rint(_div32(-mn, s)) + F32(0.0)).astype(F32)   # a zero zero point is +0
     return s, zp
 
 

@@ -5,10 +5,10 @@
 // One row = head_dim bf16 values of one (token, KV head).  A row is handled by
 // D/8 consecutive lanes, each loading 16 bytes (8 values) and storing 8 codes
 // (8 bytes; 4 bytes for INT4).  INT4 finds the row's min / max with xor
-// shuffles inside the lane group, and the group's first lane stores the
-// (scale, zero point) pair.  Blocks in y = 0 encode K, y = 1 encode V, so a
-// launch streams both tensors; the element format is a per-launch switch that
-// is uniform across the grid.
+// moves inside the lane group, and the group's first lane stores the (scale,
+// zero point) pair.  Blocks in y = 0 encode K, y = 1 encode V, so a launch
+// streams both tensors; each workgroup switches once on its side's element
+// format into a path specialised for it.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -29,74 +29,131 @@ struct RowSide {
   int dtype;
 };
 
-// Encode the 8 values this lane holds (x[0..7], elements [8*j, 8*j+8) of the row)
-// and store them into the destination row.
-template <int D, int LPR>
-__device__ __forceinline__ void encode_store(const float (&x)[8], int dtype, float s,
-                                             uint8_t* dst_row, float* meta_row, int j) {
-  if (dtype == DT_BF16) {
-    // unreachable: bf16 rows are copied by the caller
-    return;
+// ---------------------------------------------------------------------------
+// cross-lane moves inside the aligned group of LPR lanes that holds a row
+// ---------------------------------------------------------------------------
+
+// the value of lane (this lane xor M), for M = 1, 2 (DPP quad permutes) and
+// 4, 8 (LDS-crossbar swizzles, no address operand)
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);   // swap groups of 4
+  else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);                        // swap groups of 8
+}
+template <int M>
+__device__ __forceinline__ double xor_lane(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xor_lane<M>((uint32_t)u), hi = xor_lane<M>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+// max / min over the row's LPR lanes (8 or 16, aligned), by DPP moves: within
+// quads, then half-rows (lane i with 7 - i), then rows (i with 15 - i)
+template <int LPR>
+__device__ __forceinline__ void row_min_max(float& mn, float& mx) {
+  static_assert(LPR == 8 || LPR == 16, "lanes per row");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  using Xor1 = std::integral_constant<int, 0xB1>;   // quad_perm [1, 0, 3, 2]
+  using Xor2 = std::integral_constant<int, 0x4E>;   // quad_perm [2, 3, 0, 1]
+  using HalfMirror = std::integral_constant<int, 0x141>;
+  using Mirror = std::integral_constant<int, 0x140>;
+  mn = fminf(mn, dpp(mn, Xor1{}));
+  mx = fmaxf(mx, dpp(mx, Xor1{}));
+  mn = fminf(mn, dpp(mn, Xor2{}));
+  mx = fmaxf(mx, dpp(mx, Xor2{}));
+  mn = fminf(mn, dpp(mn, HalfMirror{}));
+  mx = fmaxf(mx, dpp(mx, HalfMirror{}));
+  if constexpr (LPR == 16) {
+    mn = fminf(mn, dpp(mn, Mirror{}));
+    mx = fmaxf(mx, dpp(mx, Mirror{}));
   }
-  if (dtype == DT_INT4) {
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-    static_assert(LPR == 8 || LPR == 16, "lanes per row");
-    // over the LPR lanes of the row (8 or 16, aligned): within quads, then
-    // half-rows (lane i with 7 - i), then rows (i with 15 - i), by DPP moves
-    // rather than LDS permutes
-    auto dpp = [](float v, auto ctrl) {
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
-    };
-    using Xor1 = std::integral_constant<int, 0xB1>;   // quad_perm [1, 0, 3, 2]
-    using Xor2 = std::integral_constant<int, 0x4E>;   // quad_perm [2, 3, 0, 1]
-    using HalfMirror = std::integral_constant<int, 0x141>;
-    using Mirror = std::integral_constant<int, 0x140>;
-    mn = fminf(mn, dpp(mn, Xor1{}));
-    mx = fmaxf(mx, dpp(mx, Xor1{}));
-    mn = fminf(mn, dpp(mn, Xor2{}));
-    mx = fmaxf(mx, dpp(mx, Xor2{}));
-    mn = fminf(mn, dpp(mn, HalfMirror{}));
-    mx = fmaxf(mx, dpp(mx, HalfMirror{}));
-    if constexpr (LPR == 16) {
-      mn = fminf(mn, dpp(mn, Mirror{}));
-      mx = fmaxf(mx, dpp(mx, Mirror{}));
-    }
-    float sc = (mx - mn) / 15.0f;
-    if (sc == 0.0f || !(fabsf(sc) <= 3.402823466e38f)) sc = (mn != 0.0f) ? fabsf(mn) : 1.0f;
-    const float zp = rintf(-mn / sc);
-    const Quot qt(sc);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = rintf(qt(x[i])) + zp;
-      q = fminf(fmaxf(q, 0.0f), 15.0f);
-      packed |= ((uint32_t)q) << (4 * i);
-    }
-    *reinterpret_cast<uint32_t*>(dst_row + 4 * j) = packed;
-    if (j == 0) *reinterpret_cast<float2*>(meta_row) = make_float2(sc, zp);
-    return;
-  }
+}
+
+// ---------------------------------------------------------------------------
+// encoders of the 8 values a lane holds (x[i] = element 8 j + i of the row)
+// ---------------------------------------------------------------------------
+
+// INT8 / FP8 codes with the tensor's (or head's) scale s: 8 bytes
+template <int DT>
+__device__ __forceinline__ uint2 encode_8bit(const float (&x)[8], float s) {
   const Quot qt(s);
   float t[2][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i / 4][i % 4] = qt(x[i]);
   uint32_t lo = 0, hi = 0;
-  if (dtype == DT_INT8) {
+  if constexpr (DT == DT_INT8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lo |= enc_int8(t[0][i]) << (8 * i);
       hi |= enc_int8(t[1][i]) << (8 * i);
     }
-  } else if (dtype == DT_E4M3) {
-    lo = enc_fp8x4<DT_E4M3>(t[0]);
-    hi = enc_fp8x4<DT_E4M3>(t[1]);
   } else {
-    lo = enc_fp8x4<DT_E5M2>(t[0]);
-    hi = enc_fp8x4<DT_E5M2>(t[1]);
+    lo = enc_fp8x4<DT>(t[0]);
+    hi = enc_fp8x4<DT>(t[1]);
   }
-  *reinterpret_cast<uint2*>(dst_row + 8 * j) = make_uint2(lo, hi);
+  return make_uint2(lo, hi);
+}
+
+// fl(a / 15), correctly rounded: one Markstein step from the correctly rounded
+// reciprocal of 15 (0x3D888889) when a is large enough for no step to
+// underflow; a true division otherwise.  Infinite or NaN a gives inf or NaN.
+__device__ __forceinline__ float div15(float a) {
+  if (!(fabsf(a) >= 0x1p-100f) || !(fabsf(a) <= 0x1p100f)) return a / 15.0f;
+  const float r = __uint_as_float(0x3D888889u);
+  const float q0 = a * r;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 15.0f, a), r, q0);
+}
+
+// INT4 asymmetric codes of the row: s = (max - min) / 15 (|min| or 1 for a
+// constant row), zp = RNE(-min / s) (+0 when zero), q = clamp(RNE(x / s) + zp,
+// 0, 15), every
+// quotient the correctly rounded float32 one; NaN elements are left out of
+// min / max and get code 0.  Returns the 8 nibbles (even element low); the
+// row's (s, zp) in *s_out, *zp_out.
+template <int LPR>
+__device__ __forceinline__ uint32_t encode_int4(const float (&x)[8], float* s_out, float* zp_out) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+  row_min_max<LPR>(mn, mx);
+  float sc = div15(mx - mn);
+  if (sc == 0.0f || !(fabsf(sc) <= 3.402823466e38f)) sc = (mn != 0.0f) ? fabsf(mn) : 1.0f;
+  const Quot qt(sc);
+  // + 0: a zero zero point is +0 whichever zero the row minimum came out as
+  // (the minimum of a row holding both -0 and +0 depends on the order)
+  const float zp = rintf(qt(-mn)) + 0.0f;
+  float q[8];
+  if (qt.fast) {
+    // with a normal scale only the upper half of the quotient's range test is
+    // kept: below 2^-60 both the corrected and the uncorrected quotient round to
+    // 0, so the code is the same; above 2^60 (an infinite x among them, whose
+    // correction would be inf - inf) the uncorrected one saturates the code
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = x[i] * qt.r;
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, sc, x[i]), qt.r, q0);
+      q[i] = rintf(fabsf(q0) <= 0x1p60f ? q1 : q0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = rintf(x[i] / sc);
+  }
+  // codes in [0, 15] (fmaxf takes a NaN to 0); pairs (even, odd) as the exact
+  // byte value even + 16 odd
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float e = fminf(fmaxf(q[i] + zp, 0.0f), 15.0f);
+    const float o = fminf(fmaxf(q[i + 1] + zp, 0.0f), 15.0f);
+    packed = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(o, 16.0f, e), i / 2, packed);
+  }
+  *s_out = sc;
+  *zp_out = zp;
+  return packed;
 }
 
 // bf16 bits of a float64 value, rounded once to nearest even.  The value is
@@ -121,6 +178,15 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
 // magnitudes span less than 2^38 (bf16 values carry 8 significant bits; D <=
 // 128 terms add 7 more), then rounded once to bf16 (returned as float32).  An
 // exact zero comes out as +0.
+template <int M>
+__device__ __forceinline__ void hadamard_lane_stage(double (&y)[8], int j) {
+  const bool upper = j & M;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double other = xor_lane<M>(y[i]);
+    y[i] = upper ? other - y[i] : y[i] + other;
+  }
+}
 template <int LPR>
 __device__ __forceinline__ void hadamard_row(float (&x)[8], int j) {
   double y[8];
@@ -135,15 +201,10 @@ __device__ __forceinline__ void hadamard_row(float (&x)[8], int j) {
         y[i] = a + b;
         y[i + h] = a - b;
       }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {
-    const bool upper = j & m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double other = __shfl_xor(y[i], m, 64);
-      y[i] = upper ? other - y[i] : y[i] + other;
-    }
-  }
+  hadamard_lane_stage<1>(y, j);
+  hadamard_lane_stage<2>(y, j);
+  hadamard_lane_stage<4>(y, j);
+  if constexpr (LPR == 16) hadamard_lane_stage<8>(y, j);
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(f64_to_bf16_rne(y[i] + 0.0));
 }
@@ -154,51 +215,54 @@ struct RowIn {
   float s;
 };
 
-template <int D>
+template <int D, int DT>
 __device__ __forceinline__ RowIn load_row(const RowSide& sd, const uint16_t* src_row, int h, int j) {
   RowIn in;
   in.raw = *reinterpret_cast<const uint4*>(src_row + 8 * j);
-  in.s = sd.scale ? sd.scale[sd.scale_per_head ? h : 0] : 1.0f;
+  if constexpr (DT == DT_INT8 || DT == DT_E4M3 || DT == DT_E5M2)
+    in.s = sd.scale ? sd.scale[sd.scale_per_head ? h : 0] : 1.0f;
+  else
+    in.s = 1.0f;
   return in;
 }
 
-template <int D>
+// encode the lane's 8 values of a row and store them at row dst_row_idx of the pages
+template <int D, int DT>
 __device__ __forceinline__ void store_row(const RowSide& sd, const RowIn& in, int64_t dst_row_idx, int j) {
   constexpr int LPR = D / 8;
   const uint4 raw = in.raw;
-  if (sd.dtype == DT_BF16) {
+  if constexpr (DT == DT_BF16) {
     *reinterpret_cast<uint4*>(sd.pages + dst_row_idx * (2 * D) + 16 * j) = raw;
-    return;
-  }
-  float x[8];
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  } else {
+    float x[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+    if constexpr (DT == DT_INT4 || DT == DT_INT4H) {
+      if constexpr (DT == DT_INT4H) hadamard_row<LPR>(x, j);
+      float sc, zp;
+      const uint32_t packed = encode_int4<LPR>(x, &sc, &zp);
+      *reinterpret_cast<uint32_t*>(sd.pages + dst_row_idx * (D / 2) + 4 * j) = packed;
+      if (j == 0) *reinterpret_cast<float2*>(sd.meta + dst_row_idx * 2) = make_float2(sc, zp);
+    } else {
+      *reinterpret_cast<uint2*>(sd.pages + dst_row_idx * D + 8 * j) = encode_8bit<DT>(x, in.s);
+    }
   }
-  int dt = sd.dtype;
-  if (dt == DT_INT4H) {   // uniform per launch side: every lane of the row takes it
-    hadamard_row<LPR>(x, j);
-    dt = DT_INT4;
-  }
-  const int rb = (dt == DT_INT4) ? D / 2 : D;
-  encode_store<D, LPR>(x, dt, in.s, sd.pages + dst_row_idx * rb,
-                       sd.meta ? sd.meta + dst_row_idx * 2 : nullptr, j);
 }
 
 // Each lane takes kRowsPerLane rows (kRowsPerLane x 16 bytes in flight before any
 // encode); the rows of one pass are consecutive, the passes of a workgroup too.
 constexpr int kRowsPerLane = 4;
 
-// R32: the row count fits 31 bits, so (token, head) come from a 32-bit division
-template <int D, bool R32>
-__global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSide v, const int64_t* slots,
-                                                               int64_t T, int Hkv, int64_t num_slots,
-                                                               int32_t* err) {
+// rows of a workgroup for the cache write, format DT known at compile time
+template <int D, bool R32, int DT>
+__device__ __forceinline__ void write_rows(const RowSide& sd, const int64_t* slots, int64_t T, int Hkv,
+                                           int64_t num_slots, int32_t* err) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kThreads / LPR;  // rows per pass
-  const RowSide& sd = (blockIdx.y == 0) ? k : v;
   const int j = threadIdx.x % LPR;
   const int64_t rows = T * Hkv;
   const int64_t row0 = (int64_t)blockIdx.x * RPB * kRowsPerLane + threadIdx.x / LPR;
@@ -219,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSid
       t = rr / Hkv;
       h = (int)(rr % Hkv);
     }
-    in[u] = load_row<D>(sd, sd.src + rr * D, h, j);
+    in[u] = load_row<D, DT>(sd, sd.src + rr * D, h, j);
     slot[u] = row < rows ? slots[t] : -1;
     hh[u] = h;
   }
@@ -232,16 +296,33 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSid
       continue;
     }
     const int64_t blk = sl / 16, off = sl % 16;
-    store_row<D>(sd, in[u], (blk * Hkv + hh[u]) * 16 + off, j);
+    store_row<D, DT>(sd, in[u], (blk * Hkv + hh[u]) * 16 + off, j);
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v, int first_block, int n_blocks,
-                                                           int Hkv) {
+// R32: the row count fits 31 bits, so (token, head) come from a 32-bit division.
+// Workgroups in y = 0 write K, y = 1 V; the format switch is uniform over a
+// workgroup, so each takes one specialised path.
+template <int D, bool R32>
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(RowSide k, RowSide v, const int64_t* slots,
+                                                               int64_t T, int Hkv, int64_t num_slots,
+                                                               int32_t* err) {
+  const RowSide& sd = (blockIdx.y == 0) ? k : v;
+  switch (sd.dtype) {
+    case DT_BF16: write_rows<D, R32, DT_BF16>(sd, slots, T, Hkv, num_slots, err); break;
+    case DT_INT8: write_rows<D, R32, DT_INT8>(sd, slots, T, Hkv, num_slots, err); break;
+    case DT_E4M3: write_rows<D, R32, DT_E4M3>(sd, slots, T, Hkv, num_slots, err); break;
+    case DT_E5M2: write_rows<D, R32, DT_E5M2>(sd, slots, T, Hkv, num_slots, err); break;
+    case DT_INT4: write_rows<D, R32, DT_INT4>(sd, slots, T, Hkv, num_slots, err); break;
+    case DT_INT4H: write_rows<D, R32, DT_INT4H>(sd, slots, T, Hkv, num_slots, err); break;
+    default: break;
+  }
+}
+
+template <int D, int DT>
+__device__ __forceinline__ void convert_rows(const RowSide& sd, int first_block, int n_blocks, int Hkv) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kThreads / LPR;
-  const RowSide& sd = (blockIdx.y == 0) ? k : v;
   const int j = threadIdx.x % LPR;
   const int64_t rows = (int64_t)n_blocks * Hkv * 16;                 // rows of the block range
   const int64_t r0 = (int64_t)blockIdx.x * RPB * kRowsPerLane + threadIdx.x / LPR;
@@ -250,13 +331,28 @@ __global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v,
   for (int u = 0; u < kRowsPerLane; ++u) {
     const int64_t r = min(r0 + (int64_t)u * RPB, rows - 1);
     const int64_t dst = (int64_t)first_block * Hkv * 16 + r;        // same slot in source and dest
-    in[u] = load_row<D>(sd, sd.src + dst * D, (int)((dst / 16) % Hkv), j);
+    in[u] = load_row<D, DT>(sd, sd.src + dst * D, (int)((dst / 16) % Hkv), j);
   }
 #pragma unroll
   for (int u = 0; u < kRowsPerLane; ++u) {
     const int64_t r = r0 + (int64_t)u * RPB;
     if (r >= rows) break;                       // uniform over the row's lanes
-    store_row<D>(sd, in[u], (int64_t)first_block * Hkv * 16 + r, j);
+    store_row<D, DT>(sd, in[u], (int64_t)first_block * Hkv * 16 + r, j);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void convert_kernel(RowSide k, RowSide v, int first_block, int n_blocks,
+                                                           int Hkv) {
+  const RowSide& sd = (blockIdx.y == 0) ? k : v;
+  switch (sd.dtype) {
+    case DT_BF16: convert_rows<D, DT_BF16>(sd, first_block, n_blocks, Hkv); break;
+    case DT_INT8: convert_rows<D, DT_INT8>(sd, first_block, n_blocks, Hkv); break;
+    case DT_E4M3: convert_rows<D, DT_E4M3>(sd, first_block, n_blocks, Hkv); break;
+    case DT_E5M2: convert_rows<D, DT_E5M2>(sd, first_block, n_blocks, Hkv); break;
+    case DT_INT4: convert_rows<D, DT_INT4>(sd, first_block, n_blocks, Hkv); break;
+    case DT_INT4H: convert_rows<D, DT_INT4H>(sd, first_block, n_blocks, Hkv); break;
+    default: break;
   }
 }
 

@@ -82,6 +82,27 @@ def test_int4_rows(D):
         assert meta_equal(gm, rm), dt
 
 
+def test_int4_scale_and_zero_point_quotients():
+    """Rows whose only nonzero entries are a (position 0) and b (position 1):
+    min and max are min(a, b, 0) and max(a, b, 0), so the row scale (max - min)
+    / 15 and the zero point -min / s sweep all positive bf16 magnitudes and
+    random differences of two bf16 values, tiny, subnormal and huge among them.
+    Codes and (s, zp) bit-exact against the oracle's IEEE divisions."""
+    rng = np.random.default_rng(23)
+    pos = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)          # every positive finite bf16
+    a = np.concatenate([pos, rng.integers(0, 0x7F80, 30000).astype(np.uint16),
+                        rng.integers(0x8000, 0xFF80, 30000).astype(np.uint16)])
+    b = np.concatenate([np.zeros(pos.size, np.uint16), rng.integers(0, 0x7F80, 30000).astype(np.uint16),
+                        rng.integers(0, 0xFF80, 30000).astype(np.uint16)])
+    rows = np.zeros((a.size, 1, 64), np.uint16)
+    rows[:, 0, 0], rows[:, 0, 1] = a, b
+    rows[:, 0, 2] = rng.integers(0, 0x3F80, a.size)       # a third, small positive entry
+    got, gm = _write_rows("int4", rows, None)
+    ref, rm = oc.encode_rows(rows, "int4")
+    assert np.array_equal(got, ref)
+    assert meta_equal(gm, rm)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_hadamard_rotate_bit_exact(D):
     """kvq_hadamard_rotate against the oracle's exact H x rounded once: bit-exact

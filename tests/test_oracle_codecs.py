@@ -213,6 +213,13 @@ def test_int4_invariants():
     assert err.max() <= 0.5 + 1e-5
 
 
+def test_int4_zero_zero_point_is_positive_zero():
+    """Rows whose minimum is a zero (either sign, or both present) store zp = +0."""
+    x = np.array([[-0.0, 0.0, 1.0, 2.0], [0.0, -0.0, 3.0, 0.5], [-0.0, -0.0, 1.0, 1.0]], np.float32)
+    _, s, zp = codecs.int4_encode_rows(x)
+    assert (zp.view(np.uint32) == 0).all()
+
+
 def test_int4_constant_rows_exact():
     x = np.array([[0.0] * 8, [3.5] * 8, [-2.25] * 8, [1e-30] * 8], np.float32)
     codes, s, zp = codecs.int4_encode_rows(x)
