@@ -156,17 +156,20 @@ __device__ __forceinline__ uint32_t encode_int4(const float (&x)[8], float* s_ou
   return packed;
 }
 
-// bf16 bits of a float64 value, rounded once to nearest even.  The value is
-// first narrowed to float32 toward zero with inexactness marked in the last bit
-// (round to odd): float32 keeps 16 bits beyond bf16's 8 at every magnitude,
-// subnormals included, so rounding that to nearest even gives the direct
-// rounding of the float64 value (a round-to-odd intermediate with at least two
-// extra bits makes the second rounding innocuous).  Past the bf16 range the
-// odd float32 maximum rounds on to infinity, as the direct rounding does.
+// bf16 bits of a float64 value, rounded once to nearest even.  The hardware
+// narrows it to the nearest float32 f (ties to even, subnormals kept); rounding
+// f to bf16 then equals rounding v itself except where f lies exactly halfway
+// between two bf16 values while v does not.  f is within half a float32 ulp of
+// v, so no such halfway point lies strictly between them: moving f one float32
+// ulp toward v makes the final rounding go v's way.  Overflow comes out as the
+// infinity the direct rounding gives, NaN as 0x7FC0.
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
-  const float f = __double2float_rz(v);
+  const float f = (float)v;
   uint32_t u = __float_as_uint(f);
-  if ((double)f != v && v == v) u |= 1u;
+  if ((u & 0xffffu) == 0x8000u) {
+    const double fd = (double)f;
+    if (fd != v && v == v) u += (fabs(v) > fabs(fd)) ? 1u : 0xffffffffu;
+  }
   return f32_to_bf16_bits(__uint_as_float(u));
 }
 

@@ -119,6 +119,9 @@ def test_hadamard_rotate_bit_exact(D):
     x[6, 2] = np.inf
     x[8, 9] = np.nan
     x[10, :2] = [np.inf, -np.inf]
+    x[11] *= np.float32(2.0 ** -130)                 # sums in the bf16 subnormal range
+    x[12] = rng.integers(-3, 4, D).astype(np.float32) * np.float32(2.0 ** -133)
+    x[13, :3] = [1.0, 2.0 ** -8, 2.0 ** -30]         # sums just off a bf16 halfway point
     wide = rng.standard_normal((200, D)).astype(np.float32)
     wide *= np.float32(2.0) ** rng.integers(-40, 40, size=wide.shape).astype(np.float32)
     bits = (x.view(np.uint32) >> 16).astype(np.uint16)
