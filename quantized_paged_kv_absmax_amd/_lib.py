@@ -7,7 +7,10 @@ import of the binding fails loudly: there is no fallback implementation.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvq.so")
+# KVQ_LIBRARY may name another build of the same C ABI (the host sanitizer build
+# lib/libkvq_hostsan.so, loaded by its test)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                          "libkvq.so")
 
 # kvq_status
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)

@@ -1,9 +1,11 @@
 """Build libkvq.so in-tree with hipcc for gfx950.
 
-    python -m quantized_paged_kv_absmax_amd.build
+    python -m quantized_paged_kv_absmax_amd.build [--host-sanitizers]
 
 Objects go to quantized_paged_kv_absmax_amd/_build/, the shared library to
-quantized_paged_kv_absmax_amd/lib/libkvq.so.  Every call rebuilds.
+quantized_paged_kv_absmax_amd/lib/libkvq.so (with --host-sanitizers,
+lib/libkvq_hostsan.so: the C ABI's host code under ASan and UBSan).  Every call
+rebuilds.
 """
 
 import os
@@ -64,9 +66,52 @@ def build(verbose=False):
     return LIB
 
 
+# Host sanitizer build: kvq_api.cpp (every argument check and the launch
+# geometry) with AddressSanitizer and UndefinedBehaviorSanitizer on its host
+# code only, linked with the ordinary device objects into lib/libkvq_hostsan.so.
+# Load it with the clang ASan runtime preloaded (host_sanitizer_runtime()) and
+# KVQ_LIBRARY pointing at it.
+HOSTSAN_LIB = os.path.join(LIBDIR, "libkvq_hostsan.so")
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def host_sanitizer_runtime():
+    """Path of the clang AddressSanitizer runtime that the sanitizer build needs preloaded."""
+    root = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(root), reverse=True) if os.path.isdir(root) else []:
+        cand = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise FileNotFoundError("clang AddressSanitizer runtime not found under " + root)
+
+
+def build_host_sanitized():
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    others = [s for s in SOURCES if s != "kvq_api.cpp"]
+    with ThreadPoolExecutor(max_workers=min(8, len(others))) as ex:
+        objs = [o for o, _ in ex.map(_compile, others)]
+    san_obj = os.path.join(BUILD, "kvq_api_hostsan.o")
+    cmd = [HIPCC, *CFLAGS, *HOSTSAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the host sanitizer build:\n{' '.join(cmd)}\n{r.stderr}")
+    tmp = HOSTSAN_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", san_obj, *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
 def clean():
     shutil.rmtree(BUILD, ignore_errors=True)
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--host-sanitizers" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose=True))

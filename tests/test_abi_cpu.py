@@ -232,3 +232,27 @@ def test_rotated_key_format_argument_errors():
     assert lib.kvq_hadamard_rotate(None, 4, 128, FAKE, None) == _lib.ERR_NULL
     assert lib.kvq_hadamard_rotate(FAKE, 4, 64, None, None) == _lib.ERR_NULL
     assert lib.kvq_hadamard_rotate(FAKE + 2, 4, 64, FAKE, None) == _lib.ERR_ALIGN
+
+
+def test_noalloc_decode_argument_checks():
+    """kvq_paged_attention_decode_noalloc rejects bad arguments, and splits whose
+    workspace exceeds its static array, on the host before any HIP call."""
+    lib = _lib.load()
+    c = _cache()
+    args = lambda **kw: dict(dict(q=FAKE, bt=FAKE, sl=FAKE, B=2, L=100, Hq=4, part=0, odt=_lib.BF16, out=FAKE), **kw)
+
+    def call(cache=c, **kw):
+        a = args(**kw)
+        return lib.kvq_paged_attention_decode_noalloc(ctypes.byref(cache) if cache is not None else None, a["q"],
+                                                      a["bt"], 8, a["sl"], a["B"], a["L"], a["Hq"], 0.088,
+                                                      a["part"], a["odt"], a["out"], None, None)
+    assert call(cache=None) == _lib.ERR_NULL
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(out=None) == _lib.ERR_NULL
+    assert call(Hq=3) == _lib.ERR_SHAPE
+    assert call(part=8) == _lib.ERR_SHAPE
+    assert call(odt=_lib.INT8) == _lib.ERR_UNSUPPORTED
+    assert call(B=0) == _lib.OK
+    big = _cache(num_kv_heads=8)
+    assert lib.kvq_decode_workspace_size(64, 64, 8, 128, 131072, 16) > _lib.DECODE_SCRATCH_BYTES
+    assert call(cache=big, B=64, L=131072, Hq=64, part=16) == _lib.ERR_WORKSPACE
