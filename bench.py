@@ -92,7 +92,7 @@ def counter_summary(csv_a, csv_b, out, command):
     for path in (csv_a, csv_b):
         tot, disp = {}, {}
         for r in csv.DictReader(open(path)):
-            m = re.search(r"decode_chunk_kernel<[^>]*, (true|false)>", r["Kernel_Name"])
+            m = re.search(r"decode_chunk_kernel<-?\d+, -?\d+, \d+, \d+, (true|false)", r["Kernel_Name"])
             if m is None:
                 continue
             wl = kernels[m.group(1) + ">"]
