@@ -77,25 +77,36 @@ def trace_summary(stats_csv, out, command):
 
 def counter_summary(csv_a, csv_b, out, command):
     """SQ counters of decode_chunk_kernel per 16-token page and KV head (the sum over
-    the waves that read it), averaged over dispatches: the one-token kernel on the
-    llama8b_int8 cache and the several-token kernel on verify16_int8's."""
+    the waves that read it), averaged over dispatches.  Each kernel instantiation is
+    matched to the workload of the same element formats, head size and query-token
+    count among those bench.py times (llama8b_int8 and another on the same formats
+    with several query tokens: verify16_int8)."""
     import csv
     import re
     from workloads import WORKLOADS, make_decode_inputs
-    kernels = {"false>": "llama8b_int8", "true>": "verify16_int8"}
-    pages = {}
-    for wl in kernels.values():
+    from quantized_paged_kv_absmax_amd import _lib
+    names = ["llama8b_int8", "verify16_int8", "fp8_e4m3", "int4", "int4_had", "bf16"]
+    kernels, pages = {}, {}
+    for wl in names:
         w = WORKLOADS[wl]
-        inp = make_decode_inputs(w)
-        pages[wl] = int(((inp.seq_lens.astype(np.int64) + 15) // 16).sum()) * w.Hkv
-    per = {}   # workload -> counter -> per-page value
+        kt = _lib.INT4_HAD if w.k_dtype == "int4h" else _lib.DTYPES[w.k_dtype]
+        key = (kt, _lib.DTYPES[w.v_dtype], w.D, w.n_q > 1)
+        kernels.setdefault(key, wl)
+    per, seen = {}, []  # workload -> counter -> per-page value
     for path in (csv_a, csv_b):
         tot, disp = {}, {}
         for r in csv.DictReader(open(path)):
-            m = re.search(r"decode_chunk_kernel<-?\d+, -?\d+, \d+, \d+, (true|false)", r["Kernel_Name"])
+            m = re.search(r"decode_chunk_kernel<(-?\d+), (-?\d+), (\d+), \d+, (true|false)", r["Kernel_Name"])
             if m is None:
                 continue
-            wl = kernels[m.group(1) + ">"]
+            wl = kernels.get((int(m.group(1)), int(m.group(2)), int(m.group(3)), m.group(4) == "true"))
+            if wl is None:
+                continue
+            if wl not in pages:
+                w = WORKLOADS[wl]
+                inp = make_decode_inputs(w)
+                pages[wl] = int(((inp.seq_lens.astype(np.int64) + 15) // 16).sum()) * w.Hkv
+                seen.append(wl)
             c = r["Counter_Name"].replace("SQ_", "")
             tot.setdefault(wl, {})
             tot[wl][c] = tot[wl].get(c, 0.0) + float(r["Counter_Value"])
@@ -107,7 +118,7 @@ def counter_summary(csv_a, csv_b, out, command):
              "  " + command, "", "kvq_paged_attention_decode source hash: " + decode_source_hash(), "",
              "Summed over the waves that read a page (the several-token kernel runs four, one per",
              "16-column tile); *_CYCLES, ACTIVE_* and WAIT_* in the counters' own units.", ""]
-    for wl in kernels.values():
+    for wl in seen:
         lines.append(f"{wl}: {pages[wl]} page-heads per call")
         for c, v in sorted(per.get(wl, {}).items()):
             lines.append(f"  {c:<28} {v:10.1f}")
