@@ -37,8 +37,9 @@ struct RowSide {
 // 4, 8 (LDS-crossbar swizzles, no address operand)
 template <int M>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
-  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  // quad permutes read a valid lane everywhere, so no old value is needed
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, true);
   else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);   // swap groups of 4
   else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);                        // swap groups of 8
 }
@@ -54,8 +55,9 @@ __device__ __forceinline__ double xor_lane(double v) {
 template <int LPR>
 __device__ __forceinline__ void row_min_max(float& mn, float& mx) {
   static_assert(LPR == 8 || LPR == 16, "lanes per row");
+  // every control below reads a valid lane of the same row: no old value needed
   auto dpp = [](float v, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, true));
   };
   using Xor1 = std::integral_constant<int, 0xB1>;   // quad_perm [1, 0, 3, 2]
   using Xor2 = std::integral_constant<int, 0x4E>;   // quad_perm [2, 3, 0, 1]
@@ -156,21 +158,21 @@ __device__ __forceinline__ uint32_t encode_int4(const float (&x)[8], float* s_ou
   return packed;
 }
 
-// bf16 bits of a float64 value, rounded once to nearest even.  The hardware
-// narrows it to the nearest float32 f (ties to even, subnormals kept); rounding
-// f to bf16 then equals rounding v itself except where f lies exactly halfway
-// between two bf16 values while v does not.  f is within half a float32 ulp of
-// v, so no such halfway point lies strictly between them: moving f one float32
-// ulp toward v makes the final rounding go v's way.  Overflow comes out as the
-// infinity the direct rounding gives, NaN as 0x7FC0.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+// A float32 whose rounding to bf16 (nearest even) equals the rounding of the
+// float64 v itself.  The hardware narrows v to the nearest float32 f (ties to
+// even, subnormals kept); rounding f to bf16 then equals rounding v except where
+// f lies exactly halfway between two bf16 values while v does not.  f is within
+// half a float32 ulp of v, so no such halfway point lies strictly between them:
+// moving f one float32 ulp toward v makes the final rounding go v's way.
+// Overflow then rounds to the infinity the direct rounding gives; NaN stays NaN.
+__device__ __forceinline__ float f64_to_f32_for_bf16(double v) {
   const float f = (float)v;
   uint32_t u = __float_as_uint(f);
   if ((u & 0xffffu) == 0x8000u) {
     const double fd = (double)f;
     if (fd != v && v == v) u += (fabs(v) > fabs(fd)) ? 1u : 0xffffffffu;
   }
-  return f32_to_bf16_bits(__uint_as_float(u));
+  return __uint_as_float(u);
 }
 
 // The unnormalised Walsh-Hadamard transform of a row held by LPR aligned lanes,
@@ -183,11 +185,14 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
 // exact zero comes out as +0.
 template <int M>
 __device__ __forceinline__ void hadamard_lane_stage(double (&y)[8], int j) {
-  const bool upper = j & M;
+  // the lower lane of a pair keeps y + other, the upper other - y: one fma with
+  // a factor of +-1, rounded once like the add or subtraction it stands for
+  // (zeros included: x + (-x) is +0 either way)
+  const double sgn = (j & M) ? -1.0 : 1.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const double other = xor_lane<M>(y[i]);
-    y[i] = upper ? other - y[i] : y[i] + other;
+    y[i] = __builtin_fma(sgn, y[i], other);
   }
 }
 template <int LPR>
@@ -208,8 +213,16 @@ __device__ __forceinline__ void hadamard_row(float (&x)[8], int j) {
   hadamard_lane_stage<2>(y, j);
   hadamard_lane_stage<4>(y, j);
   if constexpr (LPR == 16) hadamard_lane_stage<8>(y, j);
+  // float64 -> float32 with the bf16 double-rounding case fixed, then the pair
+  // to bf16 by the hardware conversion (nearest even) and back to float32
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(f64_to_bf16_rne(y[i] + 0.0));
+  for (int i = 0; i < 8; i += 2) {
+    const float a = f64_to_f32_for_bf16(y[i] + 0.0), b = f64_to_f32_for_bf16(y[i + 1] + 0.0);
+    const bf16x2n v = {(__bf16)a, (__bf16)b};
+    const uint32_t w = __builtin_bit_cast(uint32_t, v);
+    x[i] = __uint_as_float(w << 16);
+    x[i + 1] = __uint_as_float(w & 0xffff0000u);
+  }
 }
 
 // this lane's 16 source bytes of a row, and the row's scale
