@@ -480,10 +480,38 @@ def cpu_baseline(min_s=8.0):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "one_thread_gbs": nbytes1 / dt1 / 1e9,
             "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "affinity": aff,
+            "write_calibrate_convert": oracle_write_rates(w, inp),
             "sample": f"oracle fp64 decode, one sequence at a time, of {done} sequence decodes "
                       f"({done / w.B:.2f} passes over the {w.B} sequences of the llama8b_int8 workload; "
                       f"{nbytes / 1e6:.1f} MB of int8 KV in {dt:.1f} s) with {threads} BLAS threads, then "
                       f"{done1} sequence decodes ({nbytes1 / 1e6:.1f} MB in {dt1:.1f} s) with one thread"}
+
+
+def oracle_write_rates(w, inp, n_tok=32768):
+    """The oracle's calibration, cache write and INT4 conversion on host cores,
+    over the first n_tok tokens of the headline workload, in GB/s of the bytes
+    each moves (bf16 read; codes and INT4 metadata written)."""
+    from oracle import cache as oc
+    k, v = inp.k_bits[:n_tok], inp.v_bits[:n_tok]
+    th = n_tok * w.Hkv
+    out = {"tokens": n_tok}
+    t0 = time.perf_counter()
+    _, ks = oc.calibrate(k, "per_tensor", 127.0)
+    _, vs = oc.calibrate(v, "per_tensor", 127.0)
+    out["calibrate_gbs"] = 2 * th * 2 * w.D / (time.perf_counter() - t0) / 1e9
+    nb = (n_tok + 15) // 16
+    slots = np.arange(n_tok, dtype=np.int64)
+    cache = oc.PagedCache(nb, w.Hkv, w.D, "int8", "int8", k_scale=ks, v_scale=vs)
+    t0 = time.perf_counter()
+    cache.write(k, v, slots)
+    out["write_int8_gbs"] = th * (2 * 2 * w.D + 2 * w.D) / (time.perf_counter() - t0) / 1e9
+    src_k = np.ascontiguousarray(k.reshape(nb, 16, w.Hkv, w.D).transpose(0, 2, 1, 3))
+    src_v = np.ascontiguousarray(v.reshape(nb, 16, w.Hkv, w.D).transpose(0, 2, 1, 3))
+    c4 = oc.PagedCache(nb, w.Hkv, w.D, "int4", "int4")
+    t0 = time.perf_counter()
+    c4.convert_from_bf16(src_k, src_v, 0, nb)
+    out["convert_int4_gbs"] = th * (2 * 2 * w.D + 2 * (w.D // 2 + 8)) / (time.perf_counter() - t0) / 1e9
+    return out
 
 
 def profile_workload(name):

@@ -83,3 +83,13 @@ def test_stale_traffic_profile_is_not_reported(tmp_path, monkeypatch):
     assert bench.read_traffic("llama8b_int8", "abc") == 123.0
     assert bench.read_traffic("llama8b_int8", "def") is None
     assert bench.read_traffic("fp8_e4m3", "abc") is None
+
+
+def test_oracle_write_rates_cover_the_three_write_side_steps():
+    from workloads import WORKLOADS, make_decode_inputs
+    w = WORKLOADS["llama8b_int8"]
+    inp = make_decode_inputs(w)
+    r = bench.oracle_write_rates(w, inp, n_tok=512)
+    assert r["tokens"] == 512
+    for k in ("calibrate_gbs", "write_int8_gbs", "convert_int4_gbs"):
+        assert r[k] > 0
