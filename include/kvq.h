@@ -22,7 +22,9 @@
  *   - Pointers marked (device) are HIP device pointers, (host) host pointers.
  *     The caller allocates and owns every buffer, including decode workspace;
  *     the library allocates nothing, keeps no pointer past the call and no state
- *     between calls, and is safe to call from several host threads.
+ *     between calls, and is safe to call from several host threads.  The one
+ *     exception is kvq_paged_attention_decode_noalloc, whose workspace is a
+ *     device array inside the library (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *     enqueues work on it and returns without synchronising; buffers must stay
  *     valid until that work has run.
