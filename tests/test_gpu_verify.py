@@ -124,3 +124,33 @@ def test_verify_many_rows(kd, vd, Hq, Hkv, D, n_q, B, lens):
         mx, bad = gate_errors(out, ref, odt)
         log(f"[verify rows {kd}/{vd} B={B} n_q={n_q} Hq={Hq} D={D}] out={odt} max|err|={mx:.3e}")
         assert bad == 0
+
+
+@pytest.mark.parametrize("B", [64, 9])
+def test_verify16_repeated_calls_bit_identical(B):
+    """The several-token kernel at the verify16_int8 shape (four waves sharing each
+    round through LDS, two barriers per round): eight calls through one workspace
+    are bit-identical, and within the oracle gate on a reduced batch.  A round read
+    before every wave's share of it had landed, or refilled before every wave had
+    read it, would change a piece from call to call."""
+    w = WORKLOADS["verify16_int8"]
+    inp = make_decode_inputs(w, B=B)
+    log(f"[verify16 repeat] B={B} lens={inp.seq_lens.tolist()[:8]}")
+    r = build_library_cache(w, inp)
+    need = kvq.kvq_verify_workspace_size(B, w.n_q, w.Hq, w.Hkv, w.D, inp.max_seq_len, 0)
+    ws = torch.full((max(need, 16),), 0x7F, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(8):
+        out = torch.full((B * w.n_q, w.Hq, w.D), float("nan"), device="cuda")
+        kvq.kvq_paged_attention_verify(r.cache, r.q, w.n_q, r.bt, r.sl, inp.max_seq_len, softmax_scale(w.D),
+                                       partition=0, workspace=ws, out_dtype="f32", out=out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    for i, out in enumerate(outs[1:], 1):
+        assert torch.equal(out, outs[0]), i
+    assert torch.isfinite(outs[0]).all()
+    if B <= 9:
+        o = build_oracle_cache(w, inp)
+        mx, nbad = gate_errors(outs[0], oracle_decode(o, inp), "f32")
+        log(f"[verify16 repeat] B={B} max|err|={mx:.3e}")
+        assert nbad == 0
