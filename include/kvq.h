@@ -231,6 +231,40 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                       void* out, int32_t* err_count, void* stream);
 
 /*
+ * kvq_paged_attention_decode_write — the decode step's two operations in one
+ * call: store each sequence's new token (vLLM issue 4025, methods item 2) and
+ * attend over the cache that includes it (methods item 3).
+ *
+ * The same as kvq_cache_write(cache, k_new, v_new, slot_mapping, batch, ...)
+ * followed by kvq_paged_attention_decode(...) with these arguments, when every
+ * slot_mapping[b] is either negative (nothing written) or the slot of position
+ * seq_lens[b] - 1 of sequence b, i.e. block_tables[b][(seq_lens[b] - 1) / 16] *
+ * 16 + (seq_lens[b] - 1) % 16: the codes stored, the output and err_count are
+ * then bit-identical to the two calls'.  For 8- and 16-bit K and V one kernel
+ * does both: the wave that reads the page holding position seq_lens[b] - 1
+ * encodes the new rows, stores them, and uses them in place of the page's stale
+ * row, so the separate write launch and its wait disappear from the step.
+ * With INT4 keys or values (whose rows need a whole-row scale and zero point
+ * first) it launches the write and then the decode.
+ *   k_new, v_new  (device) bf16 [batch][num_kv_heads][head_dim], 16-B aligned: row
+ *                 b is sequence b's new token
+ *   slot_mapping  (device) int64 [batch]
+ *   other arguments, workspace (kvq_decode_workspace_size) and errors as
+ *                 kvq_paged_attention_decode; KVQ_ERR_NULL also for a NULL
+ *                 k_new, v_new or slot_mapping when batch > 0.
+ * One-launch form, a slot that is neither negative nor that position's: it is
+ * not written and is counted once in err_count (kvq_cache_write would have
+ * written it); a sequence with seq_lens[b] <= 0 writes nothing.
+ */
+kvq_status kvq_paged_attention_decode_write(const kvq_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                                            const int64_t* slot_mapping, const uint16_t* q,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                            int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                            void* workspace, size_t workspace_bytes, int32_t out_dtype, void* out,
+                                            int32_t* err_count, void* stream);
+
+/*
  * kvq_paged_attention_decode_noalloc — kvq_paged_attention_decode without a
  * caller-supplied workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

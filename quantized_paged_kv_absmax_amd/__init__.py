@@ -13,5 +13,6 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     PagedKVCache, kvq_calibrate_scales, kvq_cache_write, kvq_convert_cache, kvq_decode_workspace_size,
     kvq_paged_attention_decode, kvq_paged_attention_verify, kvq_verify_workspace_size, kvq_cache_block_bytes,
-    kvq_blocks_in_budget, kvq_hadamard_rotate, kvq_paged_attention_decode_noalloc, row_bytes,
+    kvq_blocks_in_budget, kvq_hadamard_rotate, kvq_paged_attention_decode_noalloc, kvq_paged_attention_decode_write,
+    row_bytes,
 )

@@ -27,7 +27,7 @@ GRANULARITIES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD, "per_toke
 EXPORTS = ("kvq_calibrate_scales", "kvq_cache_write", "kvq_convert_cache", "kvq_decode_workspace_size",
            "kvq_paged_attention_decode", "kvq_paged_attention_verify", "kvq_verify_workspace_size",
            "kvq_cache_block_bytes", "kvq_blocks_in_budget", "kvq_status_string", "kvq_abi_version",
-           "kvq_hadamard_rotate", "kvq_paged_attention_decode_noalloc")
+           "kvq_hadamard_rotate", "kvq_paged_attention_decode_noalloc", "kvq_paged_attention_decode_write")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -67,6 +67,9 @@ def load():
     lib.kvq_paged_attention_decode.restype = I32
     lib.kvq_paged_attention_decode_noalloc.argtypes = [CP, P, P, I32, P, I32, I32, I32, F, I32, I32, P, P, P]
     lib.kvq_paged_attention_decode_noalloc.restype = I32
+    lib.kvq_paged_attention_decode_write.argtypes = [CP, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32,
+                                                     P, P, P]
+    lib.kvq_paged_attention_decode_write.restype = I32
     lib.kvq_paged_attention_verify.argtypes = [CP, P, I32, P, I32, P, I32, I32, I32, F, I32, P, SZ, I32, P, P, P]
     lib.kvq_paged_attention_verify.restype = I32
     lib.kvq_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]

@@ -247,14 +247,10 @@ def kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_se
                                                      partition))
 
 
-def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, softmax_scale, partition=0,
-                               workspace=None, out_dtype="bf16", out=None, err_count=None, stream=None,
-                               struct=None):
-    """Decode one query per sequence: q bf16 [B][Hq][D] -> out [B][Hq][D] (bf16 or f32).
-
-    block_tables int32 [B][max_blocks]; seq_lens int32 [B]; max_seq_len: host int.
-    A workspace is allocated here with torch when the call needs one and none is given.
-    """
+def _decode_args(cache, q, block_tables, seq_lens, max_seq_len, partition, workspace, out_dtype, out, err_count,
+                 stream):
+    """Checks of one-token decode arguments; the output (and the workspace, when
+    the call needs one and none is given) allocated on the call's stream."""
     dev = cache.k_pages.device
     _need(seq_lens, torch.int32, "seq_lens", device=dev)
     if seq_lens.dim() != 1:
@@ -279,12 +275,47 @@ def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, so
     if workspace is not None:
         _need(workspace, torch.uint8, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return B, Hq, odt, out, workspace, ws_bytes
+
+
+def kvq_paged_attention_decode(cache, q, block_tables, seq_lens, max_seq_len, softmax_scale, partition=0,
+                               workspace=None, out_dtype="bf16", out=None, err_count=None, stream=None,
+                               struct=None):
+    """Decode one query per sequence: q bf16 [B][Hq][D] -> out [B][Hq][D] (bf16 or f32).
+
+    block_tables int32 [B][max_blocks]; seq_lens int32 [B]; max_seq_len: host int.
+    A workspace is allocated here with torch when the call needs one and none is given.
+    """
+    B, Hq, odt, out, workspace, ws_bytes = _decode_args(cache, q, block_tables, seq_lens, max_seq_len, partition,
+                                                        workspace, out_dtype, out, err_count, stream)
     s = cache.struct() if struct is None else struct
     st = _lib.load().kvq_paged_attention_decode(
         ctypes.byref(s), _ptr(q), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len),
         Hq, float(softmax_scale), int(partition), _ptr(workspace), ws_bytes, odt, _ptr(out), _ptr(err_count),
         _stream(stream))
     check(st, "kvq_paged_attention_decode")
+    return out
+
+
+def kvq_paged_attention_decode_write(cache, k_new, v_new, slot_mapping, q, block_tables, seq_lens, max_seq_len,
+                                     softmax_scale, partition=0, workspace=None, out_dtype="bf16", out=None,
+                                     err_count=None, stream=None, struct=None):
+    """The decode step in one call: write each sequence's new token (k_new / v_new
+    bf16 [B][Hkv][D] at slot_mapping int64 [B]) and decode q over the cache that
+    holds it; the same as kvq_cache_write then kvq_paged_attention_decode when each
+    slot is negative or that of position seq_lens[b] - 1."""
+    B, Hq, odt, out, workspace, ws_bytes = _decode_args(cache, q, block_tables, seq_lens, max_seq_len, partition,
+                                                        workspace, out_dtype, out, err_count, stream)
+    dev = cache.k_pages.device
+    _need(k_new, torch.bfloat16, "k_new", shape=(B, cache.num_kv_heads, cache.head_dim), device=dev)
+    _need(v_new, torch.bfloat16, "v_new", shape=(B, cache.num_kv_heads, cache.head_dim), device=dev)
+    _need(slot_mapping, torch.int64, "slot_mapping", shape=(B,), device=dev)
+    s = cache.struct() if struct is None else struct
+    st = _lib.load().kvq_paged_attention_decode_write(
+        ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), B, int(max_seq_len), Hq, float(softmax_scale), int(partition),
+        _ptr(workspace), ws_bytes, odt, _ptr(out), _ptr(err_count), _stream(stream))
+    check(st, "kvq_paged_attention_decode_write")
     return out
 
 

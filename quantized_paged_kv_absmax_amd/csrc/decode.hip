@@ -49,6 +49,9 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t s)
   prm.out_f32 = a.out_f32;
   prm.out = a.out;
   prm.err = a.err;
+  prm.new_k = a.n_q == 1 ? a.new_k : nullptr;
+  prm.new_v = a.n_q == 1 ? a.new_v : nullptr;
+  prm.new_slot = a.n_q == 1 ? a.new_slot : nullptr;
 
   const int groups = (prm.n_tiles + prm.wg_waves - 1) / prm.wg_waves;   // workgroups per (chunk, KV head)
   dim3 grid(a.n_chunks * groups, c.num_kv_heads);

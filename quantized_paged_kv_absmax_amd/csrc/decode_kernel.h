@@ -85,6 +85,11 @@ struct Params {
   int n_q;           // query tokens per sequence (1: decode; more: the last n_q positions, causally)
   int n_tiles;       // 16-column MFMA tiles of the n_q * g rows of a (sequence, KV head)
   int wg_waves;      // several query tokens: waves (tiles) of a workgroup, which share its pages
+  // the step's new token, written in the same launch (one query token, 8- and
+  // 16-bit formats; null: none): bf16 rows [B][Hkv][D] and their slots [B]
+  const uint16_t* new_k;
+  const uint16_t* new_v;
+  const int64_t* new_slot;
 };
 
 // chunk kernels with several query tokens per sequence (verify.hip)
@@ -637,6 +642,13 @@ __device__ __forceinline__ uint32_t ds_u16(uint32_t a) {
   return v;
 }
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// LDS writes in the same (volatile, in-order) stream as the reads above
+__device__ __forceinline__ void ds_w32(uint32_t a, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void ds_w64(uint32_t a, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 template <typename T>
 __device__ __forceinline__ void lds_tie(T& v) { asm volatile("" : "+v"(v)); }
 
@@ -703,6 +715,8 @@ constexpr int kLast = 1 << 4;    // last round of its segment
 constexpr int kTail = 1 << 5;    // holds the sequence's last page (tokens past L are masked)
 constexpr int kWhole = 1 << 6;   // the segment is the whole sequence
 constexpr int kQBuf = 1 << 7;    // query buffer of the segment (segments alternate)
+constexpr int kNew = 1 << 8;     // the round holds the step's new token, written in this launch
+constexpr int kNewBad = 1 << 9;  // ... whose slot is not that of the sequence's last position
 
 // inclusive prefix sum over the wave by DPP moves: shifts by 1, 2, 4, 8 inside
 // each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
@@ -727,7 +741,7 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // read the round into registers, frees the stage, and the round after next is
 // issued into it before the round's arithmetic.  The page bytes are then read
 // once for all the tiles of a workgroup.
-template <int KT_DECL, int VT, int D, int CH, bool MQ>
+template <int KT_DECL, int VT, int D, int CH, bool MQ, bool NEW>
 __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // rotated keys (DT_INT4H) are INT4 codes of H k: the same pages and products,
   // with the query rotated alike when a segment's query rows are read
@@ -761,12 +775,19 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   constexpr bool V_FOLD = (VT == DT_INT8 || VT == DT_INT4);
   constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 128.0f;
   constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
+  // the step's new token written in this launch: one query token, K and V in an
+  // 8- or 16-bit format (INT4 rows need a whole-row reduction first)
+  constexpr bool FW = NEW && !MQ && !KROT && KT != DT_INT4 && VT != DT_INT4;
+  static_assert(!NEW || FW, "the new-token write: one query token, 8- and 16-bit formats");
+  // with it, each stage ends in the new token's bf16 K row [0, 256) and V row [256, 512)
+  constexpr int N_OFF = SG::STAGE;
+  constexpr int STAGE_B = SG::STAGE + (FW ? 512 : 0);
 
   // two ring stages, one LDS object each: reads of one stage then carry no
   // dependence on the DMA still filling the other; the query rows of the current
   // and the next segment sit in two dynamic-LDS buffers of p.q_slot bytes
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[SG::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[SG::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE_B];
   extern __shared__ __attribute__((aligned(16))) uint8_t qlds_all[];
   auto stage_ptr = [&](auto s_tag) -> uint8_t* {
     if constexpr (decltype(s_tag)::value == 0) return lds0;
@@ -1043,6 +1064,21 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
       }
     }
     cpg += CH;
+    // the round holding the sequence's last page holds the step's new token, at
+    // row (L - 1) % 16 of page (L - 1) / 16: its slot must be that position's
+    // (a negative slot writes nothing)
+    if constexpr (FW) {
+      if (p.new_k && (d.info & kTail)) {
+        const int64_t S = p.new_slot[d.b];
+        if (S >= 0) {
+          const int i = ((d.L - 1) >> 4) - d.pg;
+          int bid = -1;
+#pragma unroll
+          for (int ii = 0; ii < CH; ++ii) bid = (ii == i) ? d.bid[ii] : bid;
+          d.info |= (bid >= 0 && S == (int64_t)bid * 16 + ((d.L - 1) & 15)) ? kNew : kNewBad;
+        }
+      }
+    }
     return d;
   };
 
@@ -1092,6 +1128,15 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         if (mine(i * UPP + KP::NINSTR + VP::NINSTR)) dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
         const auto rvm = page_rsrc(reinterpret_cast<const uint8_t*>(vmbase) + moff, ok ? 128 : 0);
         if (mine(i * UPP + KP::NINSTR + VP::NINSTR + 1)) dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
+      }
+    }
+    // the step's new token: its bf16 K and V rows, after the pages (two more
+    // loads of the round, which the ring waits count)
+    if constexpr (FW) {
+      if (d.info & kNew) {
+        const size_t row = ((size_t)d.b * p.Hkv + kvh) * D;
+        dma4(page_rsrc(reinterpret_cast<const uint8_t*>(p.new_k + row), 2 * D), sb + N_OFF, 4 * lane);
+        dma4(page_rsrc(reinterpret_cast<const uint8_t*>(p.new_v + row), 2 * D), sb + N_OFF + 256, 4 * lane);
       }
     }
   };
@@ -1568,7 +1613,68 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     else __builtin_amdgcn_s_setprio(0);
     done4 += 4;
   };
+  // The step's new token (kNew): position L - 1 of the sequence, row (L - 1) % 16
+  // of the round's page (L - 1) / 16.  Its slot must be that position's; then
+  // its K and V rows are encoded as the cache write encodes them, stored to the
+  // pages, and written over the stale row in this round's LDS stage before the
+  // round reads it (no other wave reads that page in this launch).  A negative
+  // slot writes nothing; any other slot is counted (once, by the KV-head-0 wave)
+  // and not written.
+  auto new_token = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
+    if (d.info & kNewBad) {
+      if (p.err && kvh == 0 && lane == 0) atomicAdd(p.err, 1);
+      return;
+    }
+    const int r = (d.L - 1) & 15;
+    const int i = ((d.L - 1) >> 4) - d.pg;
+    int bid = -1;
+#pragma unroll
+    for (int ii = 0; ii < CH; ++ii) bid = (ii == i) ? d.bid[ii] : bid;
+    uint8_t* sb = stage_ptr(s_tag);
+    // this lane's 4 values of each row (lanes past D / 4 hold none)
+    const int l4 = min(lane, D / 4 - 1);
+    const uint32_t nb = lds_addr(sb + N_OFF) + 8 * l4;
+    u32x2 rk = ds_b64(nb), rv = ds_b64(nb + 256);
+    lds_fence();
+    lds_tie(rk);
+    lds_tie(rv);
+    if (lane >= D / 4) return;
+    auto put = [&](auto dt_tag, const u32x2& raw, const float* scale_p, int per_head, const uint8_t* base,
+                   uint32_t stride, uint32_t lds_page, auto page_geo) __attribute__((always_inline)) {
+      constexpr int DTX = decltype(dt_tag)::value;
+      using PG = decltype(page_geo);
+      uint8_t* g = const_cast<uint8_t*>(base) + (size_t)bid * stride + (size_t)r * PG::RB;
+      if constexpr (DTX == DT_BF16) {
+        const int byte = 8 * lane;
+        *reinterpret_cast<u32x2*>(g + byte) = raw;
+        ds_w64(lds_page + PG::at(r, byte), raw);
+      } else {
+        const float sc = scale_p ? scale_p[per_head ? kvh : 0] : 1.0f;
+        const Quot qt(sc);
+        float t[4];
+        t[0] = qt(bf16_bits_to_f32(raw[0] & 0xffffu));
+        t[1] = qt(bf16_bits_to_f32(raw[0] >> 16));
+        t[2] = qt(bf16_bits_to_f32(raw[1] & 0xffffu));
+        t[3] = qt(bf16_bits_to_f32(raw[1] >> 16));
+        uint32_t w;
+        if constexpr (DTX == DT_INT8)
+          w = enc_int8(t[0]) | (enc_int8(t[1]) << 8) | (enc_int8(t[2]) << 16) | (enc_int8(t[3]) << 24);
+        else
+          w = enc_fp8x4<DTX>(t);
+        const int byte = 4 * lane;
+        *reinterpret_cast<uint32_t*>(g + byte) = w;
+        ds_w32(lds_page + PG::at(r, byte), w);
+      }
+    };
+    put(std::integral_constant<int, KT>{}, rk, p.k_scale, p.k_scale_per_head, kbase, kstride,
+        lds_addr(sb + SG::K_OFF + i * KP::SLOT), KP{});
+    put(std::integral_constant<int, VT>{}, rv, p.v_scale, p.v_scale_per_head, vbase, vstride,
+        lds_addr(sb + SG::V_OFF + i * VP::SLOT), VP{});
+  };
   auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
+    if constexpr (FW) {
+      if (d.info & (kNew | kNewBad)) new_token(d, s_tag);
+    }
     if constexpr (!MQ) pace();   // the workgroup's barriers already keep its waves together
     if (d.info & kFirst) begin_segment(d);
     if (d.info & kTail) round(std::true_type{}, d, s_tag, after_reads);
@@ -1588,6 +1694,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   auto wait_issued = [&](const Desc<CH>& d) {
     if (!(d.info & kNp)) wait_vmcnt<0>();
     else if (MQ) wait_vmcnt_rt(my_lpr + ((d.info & kFirst) ? nq : 0));
+    else if (FW && (d.info & kNew)) wait_vmcnt_rt(SG::LPR + ((d.info & kFirst) ? nq : 0) + 2);
     else if (!(d.info & kFirst)) wait_vmcnt<SG::LPR>();
     else if (nq <= 1) wait_vmcnt<SG::LPR + 1>();
     else if (nq == 2) wait_vmcnt<SG::LPR + 2>();
@@ -1675,8 +1782,18 @@ constexpr int pages_per_round() {
 template <int KT, int VT, int D, bool MQ>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
   const int nw = MQ ? prm.wg_waves : 1;
-  hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, pages_per_round<KT, VT>(), MQ>), grid, dim3(64 * nw),
-                     2 * prm.q_slot * nw, s, prm);
+  constexpr int CH = pages_per_round<KT, VT>();
+  // the variant that also writes the step's new token (one query token, 8- and
+  // 16-bit formats); the host sends INT4 through the write kernel instead
+  if constexpr (!MQ && KT != DT_INT4 && KT != DT_INT4H && VT != DT_INT4) {
+    if (prm.new_k) {
+      hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, CH, MQ, true>), grid, dim3(64 * nw), 2 * prm.q_slot * nw, s,
+                         prm);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, CH, MQ, false>), grid, dim3(64 * nw), 2 * prm.q_slot * nw, s,
+                     prm);
   return hipGetLastError();
 }
 

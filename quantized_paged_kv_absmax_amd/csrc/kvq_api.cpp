@@ -235,7 +235,8 @@ kvq_status attention_impl(const kvq_cache* cache, const uint16_t* q, int32_t n_q
                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                           int32_t num_q_heads, float softmax_scale, int32_t partition, void* workspace,
                           size_t workspace_bytes, int32_t out_dtype, void* out, int32_t* err_count, void* stream,
-                          bool use_scratch) {
+                          bool use_scratch, const uint16_t* new_k = nullptr, const uint16_t* new_v = nullptr,
+                          const int64_t* new_slot = nullptr, bool check_only = false) {
   const kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (!kvq::decode_supported(cache->k_dtype, cache->v_dtype, cache->head_dim)) return KVQ_ERR_UNSUPPORTED;
@@ -287,9 +288,13 @@ kvq_status attention_impl(const kvq_cache* cache, const uint16_t* q, int32_t n_q
     a.ws_rec = reinterpret_cast<int32_t*>(base + lay.rec);
     a.ws_o = reinterpret_cast<float*>(base + lay.o);
   }
+  if (check_only) return KVQ_OK;
   a.out_f32 = out_dtype == KVQ_F32;
   a.out = out;
   a.err = err_count;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slot = new_slot;
   return from_hip(kvq::launch_decode(view(cache), a, static_cast<hipStream_t>(stream)));
 }
 
@@ -306,6 +311,38 @@ kvq_status kvq_paged_attention_verify(const kvq_cache* cache, const uint16_t* q,
   return attention_impl(cache, q, n_q, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
                         softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream,
                         false);
+}
+
+kvq_status kvq_paged_attention_decode_write(const kvq_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                                            const int64_t* slot_mapping, const uint16_t* q,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                            int32_t num_q_heads, float softmax_scale, int32_t partition,
+                                            void* workspace, size_t workspace_bytes, int32_t out_dtype, void* out,
+                                            int32_t* err_count, void* stream) {
+  const kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch > 0 && (!k_new || !v_new || !slot_mapping)) return KVQ_ERR_NULL;
+  if (batch > 0 && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_ERR_ALIGN;
+  // every check of the attention first, so that an invalid call enqueues nothing
+  const kvq_status sa = attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                                       num_q_heads, softmax_scale, partition, workspace, workspace_bytes, out_dtype,
+                                       out, err_count, stream, false, nullptr, nullptr, nullptr, true);
+  if (sa != KVQ_OK || batch == 0) return sa;
+  const bool int4 = cache->k_dtype == KVQ_INT4_ASYM || cache->k_dtype == KVQ_INT4_HAD ||
+                    cache->v_dtype == KVQ_INT4_ASYM;
+  if (int4) {
+    // INT4 rows need their whole-row scale and zero point first: the write, then
+    // the decode, as two launches on the stream
+    const kvq_status sw = kvq_cache_write(cache, k_new, v_new, slot_mapping, batch, err_count, stream);
+    if (sw != KVQ_OK) return sw;
+    return attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
+                          softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream,
+                          false);
+  }
+  return attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
+                        softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream, false,
+                        k_new, v_new, slot_mapping);
 }
 
 kvq_status kvq_paged_attention_decode_noalloc(const kvq_cache* cache, const uint16_t* q,

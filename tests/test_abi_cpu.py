@@ -86,6 +86,33 @@ def test_decode_argument_errors():
     assert _decode(_cache(), B=0) == _lib.OK
 
 
+def test_decode_write_argument_errors():
+    """The decode step in one call checks the new rows and slots, then every
+    argument of the decode, before anything is enqueued (for INT4 caches, whose
+    write is a launch of its own, too)."""
+    lib = _lib.load()
+
+    def dw(c, kn=FAKE, vn=FAKE, sl=FAKE, B=2, Hq=4, max_seq_len=100, partition=0, q=FAKE, out=FAKE):
+        return lib.kvq_paged_attention_decode_write(ctypes.byref(c) if c is not None else None, kn, vn, sl, q, FAKE,
+                                                    8, FAKE, B, max_seq_len, Hq, 0.088, partition, None, 0,
+                                                    _lib.BF16, out, None, None)
+
+    i4 = dict(k_dtype=_lib.INT4_ASYM, v_dtype=_lib.INT4_ASYM, k_gran=_lib.PER_TOKEN_HEAD,
+              v_gran=_lib.PER_TOKEN_HEAD, k_meta=FAKE, v_meta=FAKE)
+    for kw in ({}, i4):
+        assert dw(None) == _lib.ERR_NULL
+        assert dw(_cache(**kw), kn=None) == _lib.ERR_NULL
+        assert dw(_cache(**kw), vn=None) == _lib.ERR_NULL
+        assert dw(_cache(**kw), sl=None) == _lib.ERR_NULL
+        assert dw(_cache(**kw), kn=FAKE + 8) == _lib.ERR_ALIGN
+        assert dw(_cache(**kw), Hq=5) == _lib.ERR_SHAPE
+        assert dw(_cache(**kw), partition=24) == _lib.ERR_SHAPE
+        assert dw(_cache(**kw), q=FAKE + 2) == _lib.ERR_ALIGN
+        assert dw(_cache(**kw), out=None) == _lib.ERR_NULL
+        assert dw(_cache(**kw), max_seq_len=2000) == _lib.ERR_WORKSPACE
+        assert dw(_cache(**kw), B=0, kn=None, vn=None, sl=None) == _lib.OK
+
+
 def test_verify_argument_errors():
     lib = _lib.load()
 
