@@ -316,6 +316,16 @@ class GpuWorkload:
         if self.k_new is not None:
             self.kvq.kvq_cache_write(self.cache, self.k_new, self.v_new, self.slot_new, struct=self.structs[i % self.R])
 
+    def fused_step_ok(self):
+        """One new token per sequence and one query token: the step fits one call."""
+        return self.k_new is not None and self.w.n_q == 1 and self.k_new.shape[0] == self.w.B
+
+    def write_and_decode(self, i):
+        """The step in one call (the new token's write inside the decode launch)."""
+        self.kvq.kvq_paged_attention_decode_write(self.cache, self.k_new, self.v_new, self.slot_new, self.q, self.bt,
+                                                  self.sl, self.inp.max_seq_len, self.sm, partition=self.w.partition,
+                                                  workspace=self.ws, out=self.out, struct=self.structs[i % self.R])
+
     def decode(self, i):
         if self.w.n_q > 1:
             self.kvq.kvq_paged_attention_verify(self.cache, self.q, self.w.n_q, self.bt, self.sl, self.inp.max_seq_len,
@@ -365,21 +375,28 @@ class GpuWorkload:
         return {"tokens": int(x.shape[0]), "us": t * 1e6, "gbs": x.numel() * 2 / t / 1e9}
 
 
-def time_steps(gw, steps, warmup, with_write=True):
+def time_steps(gw, steps, warmup, with_write=True, fused=True):
     """Warmup, then K timed steps (write + decode) bracketed by synchronize and
-    one event pair; returns ms per step."""
+    one event pair; returns ms per step.  fused: the step as one call
+    (kvq_paged_attention_decode_write) where it fits, else the write and the decode."""
     torch = gw.torch
-    for i in range(warmup):
+    one = with_write and fused and gw.fused_step_ok()
+
+    def step(i):
+        if one:
+            gw.write_and_decode(i)
+            return
         if with_write:
             gw.write_new(i)
         gw.decode(i)
+
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        if with_write:
-            gw.write_new(i)
-        gw.decode(i)
+        step(i)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -560,6 +577,8 @@ def main():
           f"R={gw.R} rotating copies (gen {gw.gen_s:.1f}s)", file=sys.stderr, flush=True)
     ms_step = time_steps(gw, args.steps, args.warmup, with_write=True)
     value = gw.kv_bytes / (ms_step * 1e-3) / 1e9
+    # the same step as two calls (the write kernel, then the decode), for reference
+    ms_two = time_steps(gw, args.steps, args.warmup, with_write=True, fused=False)
     khash = decode_source_hash()
     traffic = read_traffic("llama8b_int8", khash)
     batched, single = time_decode_calls(gw)
@@ -568,7 +587,10 @@ def main():
     # write alone: the 1-token-per-sequence cache write of the step
     wt = gw._events(lambda: gw.write_new(0), 50)
     per_dtype = {"int8 (llama8b_int8)": head}
-    extras = {"llama8b_int8": dict(gw.extra, step_write_us=wt * 1e6)}
+    extras = {"llama8b_int8": dict(gw.extra, step_write_us=wt * 1e6,
+                                   step="one call: kvq_paged_attention_decode_write" if gw.fused_step_ok()
+                                   else "kvq_cache_write + kvq_paged_attention_decode",
+                                   step_two_calls_ms=ms_two)}
     del gw
     torch.cuda.empty_cache()
 
@@ -625,8 +647,9 @@ def main():
 
 
 WORKLOADS_DESC = {
-    "workload": "llama8b_int8: single-layer decode step (write 1 new token per sequence + paged decode), "
-                "Llama-3-8B attention shape, INT8 KV with per-tensor absmax scales",
+    "workload": "llama8b_int8: single-layer decode step (write 1 new token per sequence + paged decode, one "
+                "kvq_paged_attention_decode_write call), Llama-3-8B attention shape, INT8 KV with per-tensor absmax "
+                "scales",
     "batch": 64, "seq_len": "U[512,4096]", "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
     "block_size": 16, "work_split": "automatic balanced chunks (partition=0)", "kv_dtype": "int8/int8",
 }

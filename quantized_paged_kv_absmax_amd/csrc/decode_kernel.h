@@ -974,14 +974,16 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   make_window(in_regs);
 
   // ---- per-wave constants: logit and output scales ----
-  float kfac = p.sm_log2;
+  // this KV head's K and V scales (1.0 when none is set)
+  float ksc = 1.0f, vsc = 1.0f;
   if constexpr (KT == DT_INT8 || KT == DT_E4M3 || KT == DT_E5M2) {
-    if (p.k_scale) kfac *= p.k_scale[p.k_scale_per_head ? kvh : 0];
+    if (p.k_scale) ksc = p.k_scale[p.k_scale_per_head ? kvh : 0];
   }
-  float vfac = 1.0f;
   if constexpr (VT == DT_INT8 || VT == DT_E4M3 || VT == DT_E5M2) {
-    if (p.v_scale) vfac = p.v_scale[p.v_scale_per_head ? kvh : 0];
+    if (p.v_scale) vsc = p.v_scale[p.v_scale_per_head ? kvh : 0];
   }
+  float kfac = p.sm_log2 * ksc;
+  const float vfac = vsc;
   int koff[KP::NINSTR], voff[VP::NINSTR];
 #pragma unroll
   for (int t = 0; t < KP::NINSTR; ++t) koff[t] = KP::src(t, lane);
@@ -1639,8 +1641,8 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     lds_tie(rk);
     lds_tie(rv);
     if (lane >= D / 4) return;
-    auto put = [&](auto dt_tag, const u32x2& raw, const float* scale_p, int per_head, const uint8_t* base,
-                   uint32_t stride, uint32_t lds_page, auto page_geo) __attribute__((always_inline)) {
+    auto put = [&](auto dt_tag, const u32x2& raw, float sc, const uint8_t* base, uint32_t stride, uint32_t lds_page,
+                   auto page_geo) __attribute__((always_inline)) {
       constexpr int DTX = decltype(dt_tag)::value;
       using PG = decltype(page_geo);
       uint8_t* g = const_cast<uint8_t*>(base) + (size_t)bid * stride + (size_t)r * PG::RB;
@@ -1649,7 +1651,6 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         *reinterpret_cast<u32x2*>(g + byte) = raw;
         ds_w64(lds_page + PG::at(r, byte), raw);
       } else {
-        const float sc = scale_p ? scale_p[per_head ? kvh : 0] : 1.0f;
         const Quot qt(sc);
         float t[4];
         t[0] = qt(bf16_bits_to_f32(raw[0] & 0xffffu));
@@ -1666,10 +1667,8 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         ds_w32(lds_page + PG::at(r, byte), w);
       }
     };
-    put(std::integral_constant<int, KT>{}, rk, p.k_scale, p.k_scale_per_head, kbase, kstride,
-        lds_addr(sb + SG::K_OFF + i * KP::SLOT), KP{});
-    put(std::integral_constant<int, VT>{}, rv, p.v_scale, p.v_scale_per_head, vbase, vstride,
-        lds_addr(sb + SG::V_OFF + i * VP::SLOT), VP{});
+    put(std::integral_constant<int, KT>{}, rk, ksc, kbase, kstride, lds_addr(sb + SG::K_OFF + i * KP::SLOT), KP{});
+    put(std::integral_constant<int, VT>{}, rv, vsc, vbase, vstride, lds_addr(sb + SG::V_OFF + i * VP::SLOT), VP{});
   };
   auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
     if constexpr (FW) {
