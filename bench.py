@@ -533,12 +533,20 @@ def oracle_write_rates(w, inp, n_tok=32768):
 
 def profile_workload(name):
     """One workload's decode calls alone (no headline), for a rocprofv3 run whose
-    per-kernel figures then belong to that workload only."""
+    per-kernel figures then belong to that workload only.  "<workload>:step": its
+    decode step instead (the one call that writes the new token and decodes)."""
     import torch
     import quantized_paged_kv_absmax_amd as kvq
     kvq.load()
     torch.cuda.set_device(0)
+    name, _, mode = name.partition(":")
     gw = GpuWorkload(name, "cuda:0")
+    if mode == "step":
+        if not gw.fused_step_ok():
+            raise SystemExit(f"{name}: its step is not one call")
+        ms = time_steps(gw, 110, 5, with_write=True)
+        print(json.dumps({"profile_workload": name + ":step", "ms_per_step": ms, "calls": 115}))
+        return
     batched, single = time_decode_calls(gw, samples=10)
     d = call_stats(gw, batched, single)
     print(json.dumps({"profile_workload": name, "decode_us": d["decode_us"], "decode_gbs": d["decode_gbs"],
