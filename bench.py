@@ -646,6 +646,8 @@ def main():
                                "decode_reduce_kernel<128>",
                      "timing": "median over 60 event pairs, each around 10 back-to-back calls on the launch "
                                "stream (p10/p90 in per_dtype)",
+                     "note": "the paged decode alone (kvq_paged_attention_decode); value and ms_per_step time "
+                             "the whole step, the new token's write included (extra.llama8b_int8.step)",
                      "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "per_dtype": per_dtype,
