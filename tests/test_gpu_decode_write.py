@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import quantized_paged_kv_absmax_amd as kvq
-from tests.kvq_harness import _scale_plan, dev_bf16, log, softmax_scale
+from tests.kvq_harness import _scale_plan, build_oracle_cache, dev_bf16, gate_errors, log, oracle_decode, softmax_scale
 from workloads import WORKLOADS, make_calibration_set, make_decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -103,6 +103,12 @@ def test_one_call_equals_write_then_decode(name, partition):
     assert ea == eb == 0
     # and the step changed the cache: the new rows are in it
     assert not torch.equal(a.k_pages, c.k_pages)
+    if partition == 0:
+        # against the oracle's cache with every token written, and its decode
+        o = build_oracle_cache(w, inp)
+        mx, nbad = gate_errors(ob, oracle_decode(o, inp), "f32")
+        log(f"[decode_write {name}] max|err| vs oracle {mx:.3e}")
+        assert nbad == 0
 
 
 @pytest.mark.parametrize("name", ["llama8b_int8", "bf16", "tiny_int8"])
