@@ -15,7 +15,9 @@ value = algorithmic KV bytes read per step / step time (GB/s), where the KV byte
 are sum_b L_b * Hkv * (K + V bytes per token-head: 2*D for 8-bit codes).
 The JSON line also carries the decode kernel's roofline, per-dtype decode
 figures for the other workloads, cache-write / convert / calibrate GB/s, and the
-oracle's CPU throughput on a bounded sample.
+oracle's CPU throughput on a bounded sample.  Beside each decode it times a
+launch that reads the same pages and computes nothing (read_only, from
+lib/libkvq_probe.so): what one launch reaches on those pages.
 """
 
 import argparse
@@ -434,7 +436,71 @@ def time_decode_calls(gw, samples=60, batch=10, warmup=5):
     return batched, single
 
 
-def call_stats(gw, batched, single, traffic=None):
+def page_list(inp):
+    """Block ids of every page a decode reads, sequence by sequence (the order of
+    the decode's concatenated page list)."""
+    L = inp.seq_lens.astype(np.int64)
+    ids = [inp.block_tables[b, :(L[b] + 15) // 16] for b in range(len(L)) if L[b] > 0]
+    return np.concatenate(ids).astype(np.int32)
+
+
+_PROBE = []
+
+
+def _probe_fn():
+    """kvq_probe_read_pages from lib/libkvq_probe.so (built beside libkvq.so)."""
+    if not _PROBE:
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "lib", "libkvq_probe.so"))
+        f = lib.kvq_probe_read_pages
+        P = ctypes.c_void_p
+        f.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      P, P]
+        f.restype = ctypes.c_int
+        _PROBE.append(f)
+    return _PROBE[0]
+
+
+def time_read_only(gw, samples=60, batch=10):
+    """The same pages a decode call reads (K, V and INT4 metadata of each (page, KV
+    head)), read by one launch of a kernel that computes nothing
+    (libkvq_probe.so), in about the decode's number of waves (2048, a contiguous
+    run of the page list each) and timed as time_decode_calls times the decode.
+    Returns per-launch microseconds (batched samples)."""
+    torch = gw.torch
+    f = _probe_fn()
+    c, w = gw.cache, gw.w
+    lst = torch.from_numpy(page_list(gw.inp)).to(c.k_pages.device)
+    page_bytes = c.k_pages[0, 0].numel()
+    assert c.v_pages[0, 0].numel() == page_bytes, "K and V pages of one size"
+    n_chunks = -(-2048 // w.Hkv)
+    sink = torch.zeros(n_chunks * w.Hkv, dtype=torch.int32, device=c.k_pages.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        kp, vp, km, vm = gw.copies[i % gw.R]
+        st = f(kp.data_ptr(), vp.data_ptr(), None if km is None else km.data_ptr(),
+               None if vm is None else vm.data_ptr(), lst.data_ptr(), lst.numel(), w.Hkv, page_bytes, n_chunks,
+               c.num_blocks, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"kvq_probe_read_pages: hipError {st}")
+
+    for i in range(5):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    k = 0
+    for a, b in ev:
+        a.record()
+        for _ in range(batch):
+            launch(k)
+            k += 1
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 / batch for a, b in ev])
+
+
+def call_stats(gw, batched, single, traffic=None, read_only=None):
     med = float(np.median(batched))
     gbs = gw.kv_bytes / (med * 1e-6) / 1e9
     d = {"decode_us": med, "decode_us_p10_p90": [float(np.percentile(batched, 10)), float(np.percentile(batched, 90))],
@@ -443,6 +509,11 @@ def call_stats(gw, batched, single, traffic=None):
     if traffic is not None:
         d["traffic_bytes"] = traffic
         d["traffic_over_algorithmic"] = traffic / gw.kv_bytes
+    if read_only is not None:
+        r = float(np.median(read_only))
+        d["read_only_us"] = r
+        d["read_only_gbs"] = gw.kv_bytes / (r * 1e-6) / 1e9
+        d["decode_over_read_only"] = r / med
     return d
 
 
@@ -590,7 +661,7 @@ def main():
     khash = decode_source_hash()
     traffic = read_traffic("llama8b_int8", khash)
     batched, single = time_decode_calls(gw)
-    head = call_stats(gw, batched, single, traffic)
+    head = call_stats(gw, batched, single, traffic, time_read_only(gw))
     achieved = head["decode_gbs"]
     # write alone: the 1-token-per-sequence cache write of the step
     wt = gw._events(lambda: gw.write_new(0), 50)
@@ -611,7 +682,7 @@ def main():
             g2 = GpuWorkload(name, device)
             samples = 20 if name == "longctx_int8" else 40
             b2, s2 = time_decode_calls(g2, samples=samples)
-            d = call_stats(g2, b2, s2, read_traffic(name, khash))
+            d = call_stats(g2, b2, s2, read_traffic(name, khash), time_read_only(g2, samples=samples))
             per_dtype[f"{g2.w.k_dtype}/{g2.w.v_dtype} ({name})"] = d
             extras[name] = g2.extra
             print(f"[bench] {name}: decode {d['decode_us']:.1f} us, {d['decode_gbs']:.0f} GB/s", file=sys.stderr,
@@ -648,6 +719,11 @@ def main():
                                "stream (p10/p90 in per_dtype)",
                      "note": "the paged decode alone (kvq_paged_attention_decode); value and ms_per_step time "
                              "the whole step, the new token's write included (extra.llama8b_int8.step)",
+                     "read_only": {"us": round(head["read_only_us"], 2), "gbs": round(head["read_only_gbs"], 1),
+                                   "frac": round(head["read_only_gbs"] / HBM_PEAK_GBS, 4),
+                                   "decode_over_read_only": round(head["decode_over_read_only"], 4),
+                                   "what": "the same pages read by one launch of a kernel that computes nothing "
+                                           "(lib/libkvq_probe.so), 2048 waves, timed like the decode call"},
                      "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "per_dtype": per_dtype,

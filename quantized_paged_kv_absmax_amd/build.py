@@ -3,7 +3,8 @@
     python -m quantized_paged_kv_absmax_amd.build [--host-sanitizers]
 
 Objects go to quantized_paged_kv_absmax_amd/_build/, the shared library to
-quantized_paged_kv_absmax_amd/lib/libkvq.so (with --host-sanitizers,
+quantized_paged_kv_absmax_amd/lib/libkvq.so, and bench.py's page-read probe to
+lib/libkvq_probe.so (with --host-sanitizers,
 lib/libkvq_hostsan.so: the C ABI's host code under ASan and UBSan).  Every call
 rebuilds.
 """
@@ -20,6 +21,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libkvq.so")
+# a measurement aid for bench.py (a read of the decode's pages, no compute), not
+# part of libkvq.so's C ABI
+PROBE_LIB = os.path.join(LIBDIR, "libkvq_probe.so")
+PROBE_SOURCE = "read_probe.hip"
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,8 +54,9 @@ def _compile(src):
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        results = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
+    probe_obj = results.pop()[0]
     objs = [o for o, _ in results]
     if verbose:
         for (o, err) in results:
@@ -63,6 +69,12 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", probe_obj, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

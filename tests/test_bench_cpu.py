@@ -9,6 +9,7 @@ import shutil
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import bench
@@ -93,3 +94,21 @@ def test_oracle_write_rates_cover_the_three_write_side_steps():
     assert r["tokens"] == 512
     for k in ("calibrate_gbs", "write_int8_gbs", "convert_int4_gbs"):
         assert r[k] > 0
+
+
+def test_page_list_is_the_decode_order():
+    # every page of every non-empty sequence, sequence by sequence
+    class Inp:
+        seq_lens = np.array([17, 0, 16, 1], np.int32)
+        block_tables = np.array([[5, 6, 9], [1, 2, 3], [7, 8, 0], [4, 0, 0]], np.int32)
+    assert bench.page_list(Inp).tolist() == [5, 6, 7, 4]
+
+
+def test_read_probe_library_loads_and_checks_arguments():
+    # the probe's host-side checks return hipErrorInvalidValue (1) before any launch
+    f = bench._probe_fn()
+    P = 1 << 20
+    assert f(None, P, None, None, P, 10, 8, 2048, 256, 100, P, None) == 1       # no K pages
+    assert f(P, P, None, None, P, 0, 8, 2048, 256, 100, P, None) == 1           # no pages to read
+    assert f(P, P, None, None, P, 10, 8, 8192, 256, 100, P, None) == 1          # pages over 4 KB
+    assert f(P, P, None, None, P, 10, 8, 2050, 256, 100, P, None) == 1          # not a multiple of 16 bytes
