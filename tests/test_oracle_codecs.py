@@ -143,6 +143,35 @@ def test_fp8_encode_matches_torch_cast_in_range(fmt, tdt, lim):
 # ---------------------------------------------------------------------------
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_exact_ties_follow_the_quotient(fmt):
+    """x / s exactly halfway between two adjacent finite codes (x = t s exact in
+    float32: t has at most 5 significant bits, s 16) encodes to the code whose
+    mantissa LSB is 0.  A product by the rounded reciprocal, x * fl32(1 / s),
+    misses some of these ties in the last bit: the cases include such ties, so
+    only the correctly rounded quotient passes."""
+    tab = codecs.fp8_decode_table(fmt)
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    rng = np.random.default_rng(13)
+    xs, ss, want, flips = [], [], [], 0
+    for _ in range(3000):
+        c = int(rng.integers(0, top))                 # the tie between codes c and c + 1
+        t = Fraction(tab[c]) / 2 + Fraction(tab[c + 1]) / 2
+        neg = bool(rng.integers(0, 2))
+        m, e = np.frexp(np.float64(rng.uniform(0.001, 0.2)))
+        s = np.float32(np.ldexp(np.round(m * 2 ** 16) / 2 ** 16, e))
+        x = np.float32(float((-t if neg else t) * Fraction(float(s))))
+        assert Fraction(float(x)) == (-t if neg else t) * Fraction(float(s))   # an exact tie
+        code = (c if c % 2 == 0 else c + 1) | (0x80 if neg else 0)
+        xs.append(x)
+        ss.append(s)
+        want.append(code)
+        flips += int(codecs.fp8_encode_value(np.float32(x * np.float32(np.float32(1.0) / s)), fmt) != code)
+    assert flips > 0
+    got = codecs.fp8_encode(np.array(xs, np.float32), np.array(ss, np.float32), fmt)
+    assert got.tolist() == want
+
+
 def test_int8_named_cases():
     x = np.array([2.5, 3.5, -2.5, -0.5, 0.5, 1.5, 126.5, 127.5, 200.0, -127.5, -200.0, np.inf, -np.inf, np.nan], np.float32)
     want = [2, 4, -2, 0, 0, 2, 126, 127, 127, -127, -127, 127, -127, 0]
@@ -163,6 +192,29 @@ def test_int8_division_is_correctly_rounded():
     # one hand-checked quotient: 1/3 in float32
     q = codecs._div32(np.float32(1.0), np.float32(3.0))
     assert Fraction(float(q)) == Fraction(11184811, 33554432)
+
+
+def test_int8_exact_ties_follow_the_quotient():
+    """Codes at exact ties x / s = n + 1/2 (x = (n + 1/2) s exact in float32: s
+    has 16 significant bits) round to the even integer.  A product by the
+    rounded reciprocal, x * fl32(1 / s), misses some of these ties in the last
+    bit and rounds them the other way: the cases below include such ties, so
+    only the correctly rounded quotient passes."""
+    rng = np.random.default_rng(11)
+    xs, ss, want, flips = [], [], [], 0
+    for _ in range(4000):
+        m, e = np.frexp(np.float64(rng.uniform(0.001, 0.2)))
+        s = np.float32(np.ldexp(np.round(m * 2 ** 16) / 2 ** 16, e))
+        n = int(rng.integers(-127, 127))
+        x = np.float32((n + 0.5) * float(s))
+        assert Fraction(float(x)) == (n + Fraction(1, 2)) * Fraction(float(s))   # an exact tie
+        xs.append(x)
+        ss.append(s)
+        want.append(n if n % 2 == 0 else n + 1)                                   # the even neighbour
+        flips += int(np.rint(np.float32(x * np.float32(np.float32(1.0) / s))) != want[-1])
+    assert flips > 0
+    got = codecs.int8_encode(np.array(xs, np.float32), np.array(ss, np.float32))
+    assert got.tolist() == want
 
 
 def test_int8_round_trip_bound():
