@@ -172,6 +172,27 @@ def test_fp8_exact_ties_follow_the_quotient(fmt):
     assert got.tolist() == want
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_round_trip_bound(fmt):
+    """Decoding the code of x at scale s gives x back to within half the code
+    spacing at x / s, times s: relative 2^-(m+1) for normal values (m mantissa
+    bits), half a subnormal step below the normal range (plus the float32
+    roundings of the quotient and the product).  Named values: the code of 1.0
+    decodes to s itself."""
+    f = codecs.FP8_FORMATS[fmt]
+    mb, bias, maxval = f["mbits"], f["bias"], f["maxval"]
+    rng = np.random.default_rng(21)
+    for s in (np.float32(0.013), np.float32(0.25), np.float32(3.5)):
+        x = (rng.uniform(-1, 1, 40000) * maxval * s).astype(np.float32)
+        x[:100] *= np.float32(2.0 ** -12)          # some in the subnormal range
+        xh = codecs.fp8_decode(codecs.fp8_encode(x, s, fmt), s, fmt).astype(np.float64)
+        err = np.abs(xh - x.astype(np.float64))
+        bound = (np.abs(x.astype(np.float64)) * 2.0 ** -(mb + 1) + float(s) * 2.0 ** (-bias - mb)) * (1 + 2.0 ** -20)
+        assert (err <= bound).all()
+        one = 0x38 if fmt == "e4m3" else 0x3C
+        assert codecs.fp8_decode(np.array([one, one | 0x80], np.uint8), s, fmt).tolist() == [float(s), -float(s)]
+
+
 def test_int8_named_cases():
     x = np.array([2.5, 3.5, -2.5, -0.5, 0.5, 1.5, 126.5, 127.5, 200.0, -127.5, -200.0, np.inf, -np.inf, np.nan], np.float32)
     want = [2, 4, -2, 0, 0, 2, 126, 127, 127, -127, -127, 127, -127, 0]

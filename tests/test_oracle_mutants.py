@@ -73,6 +73,16 @@ MUTANTS = [
      "(c[..., 1::2] | (c[..., 0::2] << 4))", [tc.test_int4_pack_order]),
     ("int4 metadata bytes", codecs, "elem_bytes_per_row", "INT4_META_BYTES", "INT4_META_BYTES // 2",
      [tc.test_bytes_ratios]),
+    ("fp8 dequantisation divides", codecs, "fp8_decode", "return np.multiply(v, np.asarray(s, dtype=F32), dtype=F32)",
+     "return np.divide(v, np.asarray(s, dtype=F32), dtype=F32)",
+     [P(tc.test_fp8_round_trip_bound, f) for f in ("e4m3", "e5m2")]),
+    ("int8 dequantisation divides", codecs, "int8_decode",
+     "return np.multiply(np.asarray(q, dtype=np.int8).astype(F32), np.asarray(s, dtype=F32), dtype=F32)",
+     "return np.divide(np.asarray(q, dtype=np.int8).astype(F32), np.asarray(s, dtype=F32), dtype=F32)",
+     [tc.test_int8_round_trip_bound]),
+    ("int4 dequantisation adds the zero point", codecs, "int4_decode",
+     "d = np.subtract(q, np.asarray(zp, dtype=F32)[..., None], dtype=F32)",
+     "d = np.add(q, np.asarray(zp, dtype=F32)[..., None], dtype=F32)", [tc.test_int4_invariants]),
     ("bf16 narrowing truncates", codecs, "f32_to_bf16_rne", "r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)",
      "r = (u >> 16).astype(np.uint16)", [tc.test_f32_to_bf16_rne_matches_torch]),
     ("hadamard sign from i | k", codecs, "hadamard_matrix", "a = i[:, None] & i[None, :]",
@@ -88,6 +98,13 @@ MUTANTS = [
      "x = codecs.bf16_to_f32(x_bits)", [tca.test_calibrate_hand_example]),
     ("calibration of a zero group", oc, "calibrate", "s = np.where(a == 0, F32(1.0), s).astype(F32)",
      "s = s.astype(F32)", [tca.test_calibrate_zero_and_nan]),
+    ("calibration groups by token", oc, "calibrate", "groups = x.transpose(1, 0, 2).reshape(H, -1)",
+     "groups = x.reshape(H, -1)", [tca.test_calibrate_hand_example, tca.test_calibrate_order_free_and_running]),
+    ("per-head scales collapsed to head 0", oc, "_head_scale", "    return s\n", "    return np.full(H, s[0], F32)\n",
+     [P(tca.test_write_places_rows_at_slots, "int8", "int8")]),
+    ("convert slot order", oc.PagedCache, "convert_from_bf16",
+     "r = rows.transpose(0, 2, 1, 3).reshape(-1, self.H, self.D)", "r = rows.reshape(-1, self.H, self.D)",
+     [tca.test_convert_equals_write_of_every_slot]),
     ("write offset off by one", oc.PagedCache, "write", "blk, off = slots[idx] // self.bs, slots[idx] % self.bs",
      "blk, off = slots[idx] // self.bs, (slots[idx] + 1) % self.bs",
      [P(tca.test_write_places_rows_at_slots, "int8", "int8")]),
