@@ -330,6 +330,15 @@ def test_block_ratio_matches_l4_table():
         assert n8 / n16 == ratio == 2.0
 
 
+def test_blocks_in_budget_counts_whole_blocks():
+    """Only whole blocks count: one byte short of n blocks holds n - 1."""
+    per = codecs.kv_bytes_per_token_head("int8", "int8", 128) * 8 * 32 * 16    # 2 MiB a block
+    assert per == 2 << 20
+    assert codecs.blocks_in_budget(5 * per, "int8", "int8", 128, 8, 32) == 5
+    assert codecs.blocks_in_budget(5 * per - 1, "int8", "int8", 128, 8, 32) == 4
+    assert codecs.blocks_in_budget(per - 1, "int8", "int8", 128, 8, 32) == 0
+
+
 # ---- Hadamard rotation (KVarN's rotation step) ----
 
 def _bf16_bits(x):

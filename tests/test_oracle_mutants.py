@@ -83,6 +83,10 @@ MUTANTS = [
     ("int4 dequantisation adds the zero point", codecs, "int4_decode",
      "d = np.subtract(q, np.asarray(zp, dtype=F32)[..., None], dtype=F32)",
      "d = np.add(q, np.asarray(zp, dtype=F32)[..., None], dtype=F32)", [tc.test_int4_invariants]),
+    ("capacity rounds blocks up", codecs, "blocks_in_budget", "return budget_bytes // per_block",
+     "return -(-budget_bytes // per_block)", [tc.test_blocks_in_budget_counts_whole_blocks]),
+    ("capacity without the layer count", codecs, "blocks_in_budget", "* num_kv_heads * num_layers *",
+     "* num_kv_heads *", [tc.test_block_ratio_matches_l4_table, tc.test_blocks_in_budget_counts_whole_blocks]),
     ("bf16 narrowing truncates", codecs, "f32_to_bf16_rne", "r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)",
      "r = (u >> 16).astype(np.uint16)", [tc.test_f32_to_bf16_rne_matches_torch]),
     ("hadamard sign from i | k", codecs, "hadamard_matrix", "a = i[:, None] & i[None, :]",
