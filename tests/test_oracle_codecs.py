@@ -332,8 +332,8 @@ def test_block_ratio_matches_l4_table():
 
 def test_blocks_in_budget_counts_whole_blocks():
     """Only whole blocks count: one byte short of n blocks holds n - 1."""
-    per = codecs.kv_bytes_per_token_head("int8", "int8", 128) * 8 * 32 * 16    # 2 MiB a block
-    assert per == 2 << 20
+    per = codecs.kv_bytes_per_token_head("int8", "int8", 128) * 8 * 32 * 16    # 1 MiB a block
+    assert per == 1 << 20
     assert codecs.blocks_in_budget(5 * per, "int8", "int8", 128, 8, 32) == 5
     assert codecs.blocks_in_budget(5 * per - 1, "int8", "int8", 128, 8, 32) == 4
     assert codecs.blocks_in_budget(per - 1, "int8", "int8", 128, 8, 32) == 0
