@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(k, v) for k in ("bf16", "int8", "e4m3", "e5m2") for v in ("bf16", "int8", "e4m3", "e5m2")]
 PAIRS += [("int4", "int4"), ("int4h", "int4")]
-N_CASES = 40
+N_CASES = 160
 
 
 def _case(i):
