@@ -64,3 +64,68 @@ def test_random_case(i):
     mx, nbad = gate_errors(out, oracle_decode(o, inp), out_dtype)
     log(f"[sweep {i}] max|err| = {mx:.3e}")
     assert nbad == 0
+
+
+N_STEP_CASES = 60
+
+
+@pytest.mark.parametrize("i", range(N_STEP_CASES))
+def test_random_one_call_step(i):
+    """The decode step in one call on random shapes: equal, bit for bit, to the
+    write then the decode (output, pages, metadata), and within the f32 gate of
+    the oracle over the cache holding the new tokens."""
+    import quantized_paged_kv_absmax_amd as kvq
+    from tests.kvq_harness import dev_bf16, softmax_scale
+    w, _ = _case(5000 + i)
+    w = w.with_(n_q=1, new_tokens=1, from_bf16_cache=False)
+    inp = make_decode_inputs(w)
+    log(f"[step sweep {i}] {w.k_dtype}/{w.v_dtype} D={w.D} Hq={w.Hq} Hkv={w.Hkv} B={w.B} "
+        f"partition={w.partition} gran={w.k_gran} lens={inp.seq_lens.tolist()}")
+    full = build_library_cache(w, inp)          # scales, and the cache with every token written
+    L = inp.seq_lens.astype(np.int64)
+    has = np.nonzero(L > 0)[0]
+    last = inp.cu[1:][has] - 1
+    keep = np.ones(int(inp.cu[-1]), bool)
+    keep[last] = False
+    kb, vb = dev_bf16(inp.k_bits), dev_bf16(inp.v_bits)
+    sl = torch.from_numpy(inp.slot_mapping).cuda()
+    it = torch.from_numpy(np.nonzero(keep)[0]).cuda()
+    # one new token per sequence: a sequence with no tokens takes slot -1 (its row unused)
+    new_rows = np.zeros(w.B, np.int64)
+    new_rows[has] = last
+    slots = np.full(w.B, -1, np.int64)
+    slots[has] = inp.slot_mapping[last]
+    nr = torch.from_numpy(new_rows).cuda()
+    k_new, v_new = kb[nr].contiguous(), vb[nr].contiguous()
+    s_new = torch.from_numpy(slots).cuda()
+
+    def prompt_cache():
+        c = kvq.PagedKVCache(inp.num_blocks, w.Hkv, w.D, w.k_dtype, w.v_dtype, k_gran=w.k_gran, v_gran=w.v_gran)
+        for a, b in ((c.k_scale, full.cache.k_scale), (c.v_scale, full.cache.v_scale)):
+            if a is not None:
+                a.copy_(b)
+        if it.numel():
+            kvq.kvq_cache_write(c, kb[it].contiguous(), vb[it].contiguous(), sl[it].contiguous())
+        return c
+
+    a, b = prompt_cache(), prompt_cache()
+    ea = torch.zeros(1, dtype=torch.int32, device="cuda")
+    eb = torch.zeros_like(ea)
+    Lmax, sm = int(inp.max_seq_len), softmax_scale(w.D)
+    kvq.kvq_cache_write(a, k_new, v_new, s_new, err_count=ea)
+    oa = kvq.kvq_paged_attention_decode(a, full.q, full.bt, full.sl, Lmax, sm, partition=w.partition,
+                                        out_dtype="f32", err_count=ea)
+    ob = kvq.kvq_paged_attention_decode_write(b, k_new, v_new, s_new, full.q, full.bt, full.sl, Lmax, sm,
+                                              partition=w.partition, out_dtype="f32", err_count=eb)
+    torch.cuda.synchronize()
+    assert int(ea.item()) == int(eb.item()) == 0
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+    for x, y in ((a.k_pages, b.k_pages), (a.v_pages, b.v_pages), (b.k_pages, full.cache.k_pages),
+                 (b.v_pages, full.cache.v_pages)):
+        assert torch.equal(x, y)
+    for x, y in ((a.k_meta, b.k_meta), (a.v_meta, b.v_meta)):
+        if x is not None:
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    mx, nbad = gate_errors(ob, oracle_decode(build_oracle_cache(w, inp), inp), "f32")
+    log(f"[step sweep {i}] max|err| = {mx:.3e}")
+    assert nbad == 0
