@@ -741,6 +741,49 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // read the round into registers, frees the stage, and the round after next is
 // issued into it before the round's arithmetic.  The page bytes are then read
 // once for all the tiles of a workgroup.
+// The step's new token on one page (the one-call decode step): its bf16 K and V
+// rows, landed in LDS at n_lds (K at [0, 256), V at [256, 512)), are encoded as
+// the cache write encodes them and stored to their row of the pages in HBM
+// (kg, vg: the row's first byte) and over the stale row of the pages in the LDS
+// stage (k_lds, v_lds: the pages' first byte; r: the row).  Out of line: it runs
+// once per sequence end, and inlined its registers would weigh on the whole loop.
+template <int KT, int VT, int D>
+__device__ __noinline__ void store_new_rows(uint32_t n_lds, uint8_t* kg, uint8_t* vg, uint32_t k_lds, uint32_t v_lds,
+                                            int r, float ksc, float vsc, int lane) {
+  const int l4 = min(lane, D / 4 - 1);
+  u32x2 rk = ds_b64(n_lds + 8 * l4), rv = ds_b64(n_lds + 256 + 8 * l4);
+  lds_fence();
+  lds_tie(rk);
+  lds_tie(rv);
+  if (lane >= D / 4) return;
+  auto put = [&](auto dt_tag, const u32x2& raw, float sc, uint8_t* g, uint32_t lds_page) {
+    constexpr int DTX = decltype(dt_tag)::value;
+    using PG = LdsPage<DTX, D>;
+    if constexpr (DTX == DT_BF16) {
+      const int byte = 8 * lane;
+      *reinterpret_cast<u32x2*>(g + byte) = raw;
+      ds_w64(lds_page + PG::at(r, byte), raw);
+    } else {
+      const Quot qt(sc);
+      float t[4];
+      t[0] = qt(bf16_bits_to_f32(raw[0] & 0xffffu));
+      t[1] = qt(bf16_bits_to_f32(raw[0] >> 16));
+      t[2] = qt(bf16_bits_to_f32(raw[1] & 0xffffu));
+      t[3] = qt(bf16_bits_to_f32(raw[1] >> 16));
+      uint32_t w;
+      if constexpr (DTX == DT_INT8)
+        w = enc_int8(t[0]) | (enc_int8(t[1]) << 8) | (enc_int8(t[2]) << 16) | (enc_int8(t[3]) << 24);
+      else
+        w = enc_fp8x4<DTX>(t);
+      const int byte = 4 * lane;
+      *reinterpret_cast<uint32_t*>(g + byte) = w;
+      ds_w32(lds_page + PG::at(r, byte), w);
+    }
+  };
+  put(std::integral_constant<int, KT>{}, rk, ksc, kg, k_lds);
+  put(std::integral_constant<int, VT>{}, rv, vsc, vg, v_lds);
+}
+
 template <int KT_DECL, int VT, int D, int CH, bool MQ, bool NEW>
 __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // rotated keys (DT_INT4H) are INT4 codes of H k: the same pages and products,
@@ -1633,42 +1676,13 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
 #pragma unroll
     for (int ii = 0; ii < CH; ++ii) bid = (ii == i) ? d.bid[ii] : bid;
     uint8_t* sb = stage_ptr(s_tag);
-    // this lane's 4 values of each row (lanes past D / 4 hold none)
-    const int l4 = min(lane, D / 4 - 1);
-    const uint32_t nb = lds_addr(sb + N_OFF) + 8 * l4;
-    u32x2 rk = ds_b64(nb), rv = ds_b64(nb + 256);
-    lds_fence();
-    lds_tie(rk);
-    lds_tie(rv);
-    if (lane >= D / 4) return;
-    auto put = [&](auto dt_tag, const u32x2& raw, float sc, const uint8_t* base, uint32_t stride, uint32_t lds_page,
-                   auto page_geo) __attribute__((always_inline)) {
-      constexpr int DTX = decltype(dt_tag)::value;
-      using PG = decltype(page_geo);
-      uint8_t* g = const_cast<uint8_t*>(base) + (size_t)bid * stride + (size_t)r * PG::RB;
-      if constexpr (DTX == DT_BF16) {
-        const int byte = 8 * lane;
-        *reinterpret_cast<u32x2*>(g + byte) = raw;
-        ds_w64(lds_page + PG::at(r, byte), raw);
-      } else {
-        const Quot qt(sc);
-        float t[4];
-        t[0] = qt(bf16_bits_to_f32(raw[0] & 0xffffu));
-        t[1] = qt(bf16_bits_to_f32(raw[0] >> 16));
-        t[2] = qt(bf16_bits_to_f32(raw[1] & 0xffffu));
-        t[3] = qt(bf16_bits_to_f32(raw[1] >> 16));
-        uint32_t w;
-        if constexpr (DTX == DT_INT8)
-          w = enc_int8(t[0]) | (enc_int8(t[1]) << 8) | (enc_int8(t[2]) << 16) | (enc_int8(t[3]) << 24);
-        else
-          w = enc_fp8x4<DTX>(t);
-        const int byte = 4 * lane;
-        *reinterpret_cast<uint32_t*>(g + byte) = w;
-        ds_w32(lds_page + PG::at(r, byte), w);
-      }
-    };
-    put(std::integral_constant<int, KT>{}, rk, ksc, kbase, kstride, lds_addr(sb + SG::K_OFF + i * KP::SLOT), KP{});
-    put(std::integral_constant<int, VT>{}, rv, vsc, vbase, vstride, lds_addr(sb + SG::V_OFF + i * VP::SLOT), VP{});
+    if constexpr (FW) {
+      store_new_rows<KT, VT, D>(lds_addr(sb + N_OFF),
+                                const_cast<uint8_t*>(kbase) + (size_t)bid * kstride + (size_t)r * KP::RB,
+                                const_cast<uint8_t*>(vbase) + (size_t)bid * vstride + (size_t)r * VP::RB,
+                                lds_addr(sb + SG::K_OFF + i * KP::SLOT), lds_addr(sb + SG::V_OFF + i * VP::SLOT), r, ksc,
+                                vsc, lane);
+    }
   };
   auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
     if constexpr (FW) {
