@@ -746,7 +746,9 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // the cache write encodes them and stored to their row of the pages in HBM
 // (kg, vg: the row's first byte) and over the stale row of the pages in the LDS
 // stage (k_lds, v_lds: the pages' first byte; r: the row).  Out of line: it runs
-// once per sequence end, and inlined its registers would weigh on the whole loop.
+// once per sequence end, and inlined its registers would weigh on the whole loop
+// (the call's entry waits for the wave's loads in flight, the next round's pages
+// among them).
 template <int KT, int VT, int D>
 __device__ __noinline__ void store_new_rows(uint32_t n_lds, uint8_t* kg, uint8_t* vg, uint32_t k_lds, uint32_t v_lds,
                                             int r, float ksc, float vsc, int lane) {
