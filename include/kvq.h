@@ -242,8 +242,8 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
  * 16 + (seq_lens[b] - 1) % 16: the codes stored, the output and err_count are
  * then bit-identical to the two calls'.  For 8- and 16-bit K and V one kernel
  * does both: the wave that reads the page holding position seq_lens[b] - 1
- * encodes the new rows, stores them, and uses them in place of the page's stale
- * row, so the separate write launch and its wait disappear from the step.
+ * encodes the new rows and stores them before it reads its first page, so the
+ * separate write launch and its wait disappear from the step.
  * With INT4 keys or values (whose rows need a whole-row scale and zero point
  * first) it launches the write and then the decode.
  *   k_new, v_new  (device) bf16 [batch][num_kv_heads][head_dim], 16-B aligned: row

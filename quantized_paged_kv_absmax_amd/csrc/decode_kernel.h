@@ -715,8 +715,6 @@ constexpr int kLast = 1 << 4;    // last round of its segment
 constexpr int kTail = 1 << 5;    // holds the sequence's last page (tokens past L are masked)
 constexpr int kWhole = 1 << 6;   // the segment is the whole sequence
 constexpr int kQBuf = 1 << 7;    // query buffer of the segment (segments alternate)
-constexpr int kNew = 1 << 8;     // the round holds the step's new token, written in this launch
-constexpr int kNewBad = 1 << 9;  // ... whose slot is not that of the sequence's last position
 
 // inclusive prefix sum over the wave by DPP moves: shifts by 1, 2, 4, 8 inside
 // each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
@@ -741,30 +739,20 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // read the round into registers, frees the stage, and the round after next is
 // issued into it before the round's arithmetic.  The page bytes are then read
 // once for all the tiles of a workgroup.
-// The step's new token on one page (the one-call decode step): its bf16 K and V
-// rows, landed in LDS at n_lds (K at [0, 256), V at [256, 512)), are encoded as
-// the cache write encodes them and stored to their row of the pages in HBM
-// (kg, vg: the row's first byte) and over the stale row of the pages in the LDS
-// stage (k_lds, v_lds: the pages' first byte; r: the row).  Out of line: it runs
-// once per sequence end, and inlined its registers would weigh on the whole loop
-// (the call's entry waits for the wave's loads in flight, the next round's pages
-// among them).
+// The step's new token of one sequence and KV head (the one-call decode step):
+// its bf16 K and V rows (src_k, src_v: D values each) encoded as the cache write
+// encodes them and stored to their rows of the pages (dst_k, dst_v).  Lanes below
+// D / 4 take 4 values each.
 template <int KT, int VT, int D>
-__device__ __noinline__ void store_new_rows(uint32_t n_lds, uint8_t* kg, uint8_t* vg, uint32_t k_lds, uint32_t v_lds,
-                                            int r, float ksc, float vsc, int lane) {
-  const int l4 = min(lane, D / 4 - 1);
-  u32x2 rk = ds_b64(n_lds + 8 * l4), rv = ds_b64(n_lds + 256 + 8 * l4);
-  lds_fence();
-  lds_tie(rk);
-  lds_tie(rv);
+__device__ __forceinline__ void store_new_rows(const uint16_t* src_k, const uint16_t* src_v, uint8_t* dst_k,
+                                               uint8_t* dst_v, float ksc, float vsc, int lane) {
   if (lane >= D / 4) return;
-  auto put = [&](auto dt_tag, const u32x2& raw, float sc, uint8_t* g, uint32_t lds_page) {
+  const u32x2 rk = *reinterpret_cast<const u32x2*>(src_k + 4 * lane);
+  const u32x2 rv = *reinterpret_cast<const u32x2*>(src_v + 4 * lane);
+  auto put = [&](auto dt_tag, const u32x2& raw, float sc, uint8_t* g) __attribute__((always_inline)) {
     constexpr int DTX = decltype(dt_tag)::value;
-    using PG = LdsPage<DTX, D>;
     if constexpr (DTX == DT_BF16) {
-      const int byte = 8 * lane;
-      *reinterpret_cast<u32x2*>(g + byte) = raw;
-      ds_w64(lds_page + PG::at(r, byte), raw);
+      *reinterpret_cast<u32x2*>(g + 8 * lane) = raw;
     } else {
       const Quot qt(sc);
       float t[4];
@@ -777,13 +765,11 @@ __device__ __noinline__ void store_new_rows(uint32_t n_lds, uint8_t* kg, uint8_t
         w = enc_int8(t[0]) | (enc_int8(t[1]) << 8) | (enc_int8(t[2]) << 16) | (enc_int8(t[3]) << 24);
       else
         w = enc_fp8x4<DTX>(t);
-      const int byte = 4 * lane;
-      *reinterpret_cast<uint32_t*>(g + byte) = w;
-      ds_w32(lds_page + PG::at(r, byte), w);
+      *reinterpret_cast<uint32_t*>(g + 4 * lane) = w;
     }
   };
-  put(std::integral_constant<int, KT>{}, rk, ksc, kg, k_lds);
-  put(std::integral_constant<int, VT>{}, rv, vsc, vg, v_lds);
+  put(std::integral_constant<int, KT>{}, rk, ksc, dst_k);
+  put(std::integral_constant<int, VT>{}, rv, vsc, dst_v);
 }
 
 template <int KT_DECL, int VT, int D, int CH, bool MQ, bool NEW>
@@ -824,9 +810,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // 8- or 16-bit format (INT4 rows need a whole-row reduction first)
   constexpr bool FW = NEW && !MQ && !KROT && KT != DT_INT4 && VT != DT_INT4;
   static_assert(!NEW || FW, "the new-token write: one query token, 8- and 16-bit formats");
-  // with it, each stage ends in the new token's bf16 K row [0, 256) and V row [256, 512)
-  constexpr int N_OFF = SG::STAGE;
-  constexpr int STAGE_B = SG::STAGE + (FW ? 512 : 0);
+  constexpr int STAGE_B = SG::STAGE;
 
   // two ring stages, one LDS object each: reads of one stage then carry no
   // dependence on the DMA still filling the other; the query rows of the current
@@ -1111,21 +1095,6 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
       }
     }
     cpg += CH;
-    // the round holding the sequence's last page holds the step's new token, at
-    // row (L - 1) % 16 of page (L - 1) / 16: its slot must be that position's
-    // (a negative slot writes nothing)
-    if constexpr (FW) {
-      if (p.new_k && (d.info & kTail)) {
-        const int64_t S = p.new_slot[d.b];
-        if (S >= 0) {
-          const int i = ((d.L - 1) >> 4) - d.pg;
-          int bid = -1;
-#pragma unroll
-          for (int ii = 0; ii < CH; ++ii) bid = (ii == i) ? d.bid[ii] : bid;
-          d.info |= (bid >= 0 && S == (int64_t)bid * 16 + ((d.L - 1) & 15)) ? kNew : kNewBad;
-        }
-      }
-    }
     return d;
   };
 
@@ -1175,15 +1144,6 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         if (mine(i * UPP + KP::NINSTR + VP::NINSTR)) dma4(rkm, sb + SG::M_OFF + i * 512, 4 * lane);
         const auto rvm = page_rsrc(reinterpret_cast<const uint8_t*>(vmbase) + moff, ok ? 128 : 0);
         if (mine(i * UPP + KP::NINSTR + VP::NINSTR + 1)) dma4(rvm, sb + SG::M_OFF + i * 512 + 256, 4 * lane);
-      }
-    }
-    // the step's new token: its bf16 K and V rows, after the pages (two more
-    // loads of the round, which the ring waits count)
-    if constexpr (FW) {
-      if (d.info & kNew) {
-        const size_t row = ((size_t)d.b * p.Hkv + kvh) * D;
-        dma4(page_rsrc(reinterpret_cast<const uint8_t*>(p.new_k + row), 2 * D), sb + N_OFF, 4 * lane);
-        dma4(page_rsrc(reinterpret_cast<const uint8_t*>(p.new_v + row), 2 * D), sb + N_OFF + 256, 4 * lane);
       }
     }
   };
@@ -1660,36 +1620,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
     else __builtin_amdgcn_s_setprio(0);
     done4 += 4;
   };
-  // The step's new token (kNew): position L - 1 of the sequence, row (L - 1) % 16
-  // of the round's page (L - 1) / 16.  Its slot must be that position's; then
-  // its K and V rows are encoded as the cache write encodes them, stored to the
-  // pages, and written over the stale row in this round's LDS stage before the
-  // round reads it (no other wave reads that page in this launch).  A negative
-  // slot writes nothing; any other slot is counted (once, by the KV-head-0 wave)
-  // and not written.
-  auto new_token = [&](const Desc<CH>& d, auto s_tag) __attribute__((always_inline)) {
-    if (d.info & kNewBad) {
-      if (p.err && kvh == 0 && lane == 0) atomicAdd(p.err, 1);
-      return;
-    }
-    const int r = (d.L - 1) & 15;
-    const int i = ((d.L - 1) >> 4) - d.pg;
-    int bid = -1;
-#pragma unroll
-    for (int ii = 0; ii < CH; ++ii) bid = (ii == i) ? d.bid[ii] : bid;
-    uint8_t* sb = stage_ptr(s_tag);
-    if constexpr (FW) {
-      store_new_rows<KT, VT, D>(lds_addr(sb + N_OFF),
-                                const_cast<uint8_t*>(kbase) + (size_t)bid * kstride + (size_t)r * KP::RB,
-                                const_cast<uint8_t*>(vbase) + (size_t)bid * vstride + (size_t)r * VP::RB,
-                                lds_addr(sb + SG::K_OFF + i * KP::SLOT), lds_addr(sb + SG::V_OFF + i * VP::SLOT), r, ksc,
-                                vsc, lane);
-    }
-  };
   auto compute = [&](const Desc<CH>& d, auto s_tag, auto&& after_reads) __attribute__((always_inline)) {
-    if constexpr (FW) {
-      if (d.info & (kNew | kNewBad)) new_token(d, s_tag);
-    }
     if constexpr (!MQ) pace();   // the workgroup's barriers already keep its waves together
     if (d.info & kFirst) begin_segment(d);
     if (d.info & kTail) round(std::true_type{}, d, s_tag, after_reads);
@@ -1709,7 +1640,6 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   auto wait_issued = [&](const Desc<CH>& d) {
     if (!(d.info & kNp)) wait_vmcnt<0>();
     else if (MQ) wait_vmcnt_rt(my_lpr + ((d.info & kFirst) ? nq : 0));
-    else if (FW && (d.info & kNew)) wait_vmcnt_rt(SG::LPR + ((d.info & kFirst) ? nq : 0) + 2);
     else if (!(d.info & kFirst)) wait_vmcnt<SG::LPR>();
     else if (nq <= 1) wait_vmcnt<SG::LPR + 1>();
     else if (nq == 2) wait_vmcnt<SG::LPR + 2>();
@@ -1726,6 +1656,63 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // 256 VGPRs (one wave per SIMD), so there, as with one query token, the
   // round after next is issued once the round is done.
   constexpr bool kEarly = MQ && VT != DT_BF16;
+
+  // ---- the step's new tokens (the one-call decode step) ----
+  // Each sequence whose last page lies in this chunk takes its new token at
+  // position L - 1: row (L - 1) % 16 of page (L - 1) / 16.  Its slot must be that
+  // position's; then its K and V rows are encoded as the cache write encodes
+  // them and stored to the page before any page of the chunk is read (the page
+  // is read later by this wave alone, and a wave's memory operations to one
+  // address take effect in order; the wait below completes the stores too).  A
+  // negative slot writes nothing; any other slot is counted (once, by the
+  // KV-head-0 wave) and not written.
+  if constexpr (FW) {
+    auto write_new = [&](int b, int L) __attribute__((always_inline)) {
+      const int64_t S = p.new_slot[b];
+      if (S < 0) return;
+      const int pos = L - 1;
+      const int bb = p.block_tables[(size_t)b * p.max_blocks_per_seq + (pos >> 4)];
+      if ((uint32_t)bb >= (uint32_t)p.num_blocks || S != (int64_t)bb * 16 + (pos & 15)) {
+        if (p.err && kvh == 0 && lane == 0) atomicAdd(p.err, 1);
+        return;
+      }
+      const size_t row = ((size_t)b * p.Hkv + kvh) * D;
+      store_new_rows<KT, VT, D>(p.new_k + row, p.new_v + row,
+                                const_cast<uint8_t*>(kbase) + (size_t)bb * kstride + (size_t)(pos & 15) * KP::RB,
+                                const_cast<uint8_t*>(vbase) + (size_t)bb * vstride + (size_t)(pos & 15) * VP::RB,
+                                ksc, vsc, lane);
+    };
+    // the sequence's last page (inclusive page prefix inc, minus one) is in the chunk
+    auto ends_here = [&](int np, int inc) { return np > 0 && inc - 1 >= x0 && inc - 1 < x1; };
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (64 * r >= B) continue;
+        uint64_t m = __builtin_amdgcn_ballot_w64(64 * r + lane < B && ends_here(nr[r], ir[r]));
+        while (m) {
+          const int j = __builtin_ctzll(m);
+          m &= m - 1;
+          write_new(64 * r + j, __builtin_amdgcn_readlane(lr[r], j));
+        }
+      }
+    } else {
+      int carry = 0;
+      for (int b0 = 0; b0 < B && carry < x1; b0 += 64) {
+        const int L = load_len(b0 + lane, false);
+        const int np = (L + 15) >> 4;
+        const int inc = carry + wave_incl_sum(np);
+        uint64_t m = __builtin_amdgcn_ballot_w64(lane < B - b0 && ends_here(np, inc));
+        while (m) {
+          const int j = __builtin_ctzll(m);
+          m &= m - 1;
+          write_new(b0 + j, __builtin_amdgcn_readlane(L, j));
+        }
+        carry = __builtin_amdgcn_readlane(inc, 63);
+      }
+    }
+    wait_vmcnt<0>();
+  }
+
   Desc<CH> da = next();
   if constexpr (!kEarly) {
     if (da.info & kNp) {
