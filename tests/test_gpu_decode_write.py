@@ -140,3 +140,45 @@ def test_slots_negative_out_of_pool_and_misplaced(name):
     for x in (a, b):
         for s in (int(new[2][0]), int(new[2][b2])):
             assert torch.equal(x.k_pages[s // 16, :, s % 16], c.k_pages[s // 16, :, s % 16])
+
+
+@pytest.mark.parametrize("B", [150, 300])
+def test_one_call_with_many_short_sequences(B):
+    """Many short sequences (0 to 40 tokens): with 2048-token chunks (128 pages) a
+    chunk spans more than 64 of them, and with 300 the lengths do not fit the
+    registers, so each wave finds the sequences ending in its chunk by rescanning
+    them."""
+    from tests.kvq_harness import build_library_cache
+    lens = tuple((7 * i) % 41 for i in range(B))
+    w = WORKLOADS["llama8b_int8"].with_(B=B, lens=("fixed", lens), calib="all")
+    inp = make_decode_inputs(w)
+    full = build_library_cache(w, inp)
+    L = inp.seq_lens.astype(np.int64)
+    has = np.nonzero(L > 0)[0]
+    last = inp.cu[1:][has] - 1
+    keep = np.ones(int(inp.cu[-1]), bool)
+    keep[last] = False
+    kb, vb = dev_bf16(inp.k_bits), dev_bf16(inp.v_bits)
+    sl = torch.from_numpy(inp.slot_mapping).cuda()
+    it = torch.from_numpy(np.nonzero(keep)[0]).cuda()
+    rows = np.zeros(B, np.int64)
+    rows[has] = last
+    slots = np.full(B, -1, np.int64)
+    slots[has] = inp.slot_mapping[last]
+    nr = torch.from_numpy(rows).cuda()
+    new = (kb[nr].contiguous(), vb[nr].contiguous(), torch.from_numpy(slots).cuda())
+    c = kvq.PagedKVCache(inp.num_blocks, w.Hkv, w.D, w.k_dtype, w.v_dtype, k_gran=w.k_gran, v_gran=w.v_gran)
+    c.k_scale.copy_(full.cache.k_scale)
+    c.v_scale.copy_(full.cache.v_scale)
+    kvq.kvq_cache_write(c, kb[it].contiguous(), vb[it].contiguous(), sl[it].contiguous())
+    run = dict(q=full.q, bt=full.bt, sl=full.sl, L=int(inp.max_seq_len), sm=softmax_scale(w.D))
+    for partition in (0, 2048):
+        (oa, a, ea), (ob, b, eb) = _both(c, new, run, partition)
+        log(f"[decode_write B={B}] partition={partition}")
+        assert ea == eb == 0
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+        _same_cache(a, b)
+        assert torch.equal(b.k_pages, full.cache.k_pages) and torch.equal(b.v_pages, full.cache.v_pages)
+    mx, nbad = gate_errors(ob, oracle_decode(build_oracle_cache(w, inp), inp), "f32")
+    log(f"[decode_write B={B}] max|err| vs oracle {mx:.3e}")
+    assert nbad == 0
