@@ -211,7 +211,7 @@ def decode_source_hash():
     that a profile stays matched to its kernel across edits of comments only."""
     import re
     h = hashlib.sha256()
-    for f in ("decode_kernel.h", "decode.hip", "kvq_device.h"):
+    for f in ("decode_kernel.h", "decode.hip", "kvq_device.h", "kvq_rows.h"):
         text = open(os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)

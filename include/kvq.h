@@ -240,21 +240,21 @@ kvq_status kvq_paged_attention_decode(const kvq_cache* cache, const uint16_t* q,
  * slot_mapping[b] is either negative (nothing written) or the slot of position
  * seq_lens[b] - 1 of sequence b, i.e. block_tables[b][(seq_lens[b] - 1) / 16] *
  * 16 + (seq_lens[b] - 1) % 16: the codes stored, the output and err_count are
- * then bit-identical to the two calls'.  For 8- and 16-bit K and V one kernel
- * does both: the wave that reads the page holding position seq_lens[b] - 1
- * encodes the new rows and stores them before it reads its first page, so the
- * separate write launch and its wait disappear from the step.
- * With INT4 keys or values (whose rows need a whole-row scale and zero point
- * first) it launches the write and then the decode.
+ * then bit-identical to the two calls'.  One kernel does both: the wave that
+ * reads the page holding position seq_lens[b] - 1 encodes the new rows and
+ * stores them before it reads its first page, so the separate write launch and
+ * its wait disappear from the step (every format: INT4 rows get their scale and
+ * zero point, and rotated keys their rotation, exactly as kvq_cache_write
+ * computes them).
  *   k_new, v_new  (device) bf16 [batch][num_kv_heads][head_dim], 16-B aligned: row
  *                 b is sequence b's new token
  *   slot_mapping  (device) int64 [batch]
  *   other arguments, workspace (kvq_decode_workspace_size) and errors as
  *                 kvq_paged_attention_decode; KVQ_ERR_NULL also for a NULL
  *                 k_new, v_new or slot_mapping when batch > 0.
- * One-launch form, a slot that is neither negative nor that position's: it is
- * not written and is counted once in err_count (kvq_cache_write would have
- * written it); a sequence with seq_lens[b] <= 0 writes nothing.
+ * A slot that is neither negative nor that position's is not written and is
+ * counted once in err_count (kvq_cache_write would have written it); a
+ * sequence with seq_lens[b] <= 0 writes nothing.
  */
 kvq_status kvq_paged_attention_decode_write(const kvq_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                                             const int64_t* slot_mapping, const uint16_t* q,

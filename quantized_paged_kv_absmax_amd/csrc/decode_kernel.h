@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "kvq_device.h"
+#include "kvq_rows.h"
 #include "kvq_launch.h"
 
 namespace kvq {
@@ -772,6 +773,41 @@ __device__ __forceinline__ void store_new_rows(const uint16_t* src_k, const uint
   put(std::integral_constant<int, VT>{}, rv, vsc, dst_v);
 }
 
+// The same for INT4 K and V, with the cache write's own row encoder: lanes
+// [0, LPR) hold the K row and [LPR, 2 LPR) the V row, 8 values each (LPR = D / 8
+// aligned lanes a row, as in the write kernel); a rotated K row (ROT) is rotated
+// first.  The row's codes go to dst_k / dst_v, its (scale, zero point) pair to
+// meta_k / meta_v.
+template <int D, bool ROT>
+__device__ __forceinline__ void store_new_rows_int4(const uint16_t* src_k, const uint16_t* src_v, uint8_t* dst_k,
+                                                    uint8_t* dst_v, float* meta_k, float* meta_v, int lane) {
+  constexpr int LPR = D / 8;
+  const int grp = lane / LPR, j = lane % LPR;
+  if (grp > 1) return;
+  const uint4 raw = *reinterpret_cast<const uint4*>((grp ? src_v : src_k) + 8 * j);
+  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(wd[i] & 0xffffu);
+    x[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+  }
+  if constexpr (ROT) {
+    // every lane of both rows runs the butterfly (its moves stay in the group);
+    // the V row keeps its values
+    float xr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xr[i] = x[i];
+    hadamard_row<LPR>(xr, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = grp ? x[i] : xr[i];
+  }
+  float sc, zp;
+  const uint32_t packed = encode_int4<LPR>(x, &sc, &zp);
+  *reinterpret_cast<uint32_t*>((grp ? dst_v : dst_k) + 4 * j) = packed;
+  if (j == 0) *reinterpret_cast<float2*>(grp ? meta_v : meta_k) = make_float2(sc, zp);
+}
+
 template <int KT_DECL, int VT, int D, int CH, bool MQ, bool NEW>
 __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   // rotated keys (DT_INT4H) are INT4 codes of H k: the same pages and products,
@@ -808,8 +844,8 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
   // the step's new token written in this launch: one query token, K and V in an
   // 8- or 16-bit format (INT4 rows need a whole-row reduction first)
-  constexpr bool FW = NEW && !MQ && !KROT && KT != DT_INT4 && VT != DT_INT4;
-  static_assert(!NEW || FW, "the new-token write: one query token, 8- and 16-bit formats");
+  constexpr bool FW = NEW && !MQ;
+  static_assert(!NEW || FW, "the new-token write: one query token");
   constexpr int STAGE_B = SG::STAGE;
 
   // two ring stages, one LDS object each: reads of one stage then carry no
@@ -1677,10 +1713,16 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
         return;
       }
       const size_t row = ((size_t)b * p.Hkv + kvh) * D;
-      store_new_rows<KT, VT, D>(p.new_k + row, p.new_v + row,
-                                const_cast<uint8_t*>(kbase) + (size_t)bb * kstride + (size_t)(pos & 15) * KP::RB,
-                                const_cast<uint8_t*>(vbase) + (size_t)bb * vstride + (size_t)(pos & 15) * VP::RB,
-                                ksc, vsc, lane);
+      uint8_t* dk = const_cast<uint8_t*>(kbase) + (size_t)bb * kstride + (size_t)(pos & 15) * KP::RB;
+      uint8_t* dv = const_cast<uint8_t*>(vbase) + (size_t)bb * vstride + (size_t)(pos & 15) * VP::RB;
+      if constexpr (KT == DT_INT4) {
+        // (scale, zero point) of row r of the (block, KV head) page: [block][Hkv][16][2]
+        const size_t mi = (((size_t)bb * p.Hkv + kvh) * 16 + (pos & 15)) * 2;
+        store_new_rows_int4<D, KROT>(p.new_k + row, p.new_v + row, dk, dv, const_cast<float*>(p.k_meta) + mi,
+                                     const_cast<float*>(p.v_meta) + mi, lane);
+      } else {
+        store_new_rows<KT, VT, D>(p.new_k + row, p.new_v + row, dk, dv, ksc, vsc, lane);
+      }
     };
     // the sequence's last page (inclusive page prefix inc, minus one) is in the chunk
     auto ends_here = [&](int np, int inc) { return np > 0 && inc - 1 >= x0 && inc - 1 < x1; };
@@ -1785,9 +1827,8 @@ template <int KT, int VT, int D, bool MQ>
 hipError_t launch_typed(const Params& prm, dim3 grid, hipStream_t s) {
   const int nw = MQ ? prm.wg_waves : 1;
   constexpr int CH = pages_per_round<KT, VT>();
-  // the variant that also writes the step's new token (one query token, 8- and
-  // 16-bit formats); the host sends INT4 through the write kernel instead
-  if constexpr (!MQ && KT != DT_INT4 && KT != DT_INT4H && VT != DT_INT4) {
+  // the variant that also writes the step's new token (one query token)
+  if constexpr (!MQ) {
     if (prm.new_k) {
       hipLaunchKernelGGL((decode_chunk_kernel<KT, VT, D, CH, MQ, true>), grid, dim3(64 * nw), 2 * prm.q_slot * nw, s,
                          prm);

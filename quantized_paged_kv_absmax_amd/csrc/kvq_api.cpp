@@ -329,17 +329,6 @@ kvq_status kvq_paged_attention_decode_write(const kvq_cache* cache, const uint16
                                        num_q_heads, softmax_scale, partition, workspace, workspace_bytes, out_dtype,
                                        out, err_count, stream, false, nullptr, nullptr, nullptr, true);
   if (sa != KVQ_OK || batch == 0) return sa;
-  const bool int4 = cache->k_dtype == KVQ_INT4_ASYM || cache->k_dtype == KVQ_INT4_HAD ||
-                    cache->v_dtype == KVQ_INT4_ASYM;
-  if (int4) {
-    // INT4 rows need their whole-row scale and zero point first: the write, then
-    // the decode, as two launches on the stream
-    const kvq_status sw = kvq_cache_write(cache, k_new, v_new, slot_mapping, batch, err_count, stream);
-    if (sw != KVQ_OK) return sw;
-    return attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
-                          softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream,
-                          false);
-  }
   return attention_impl(cache, q, 1, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, num_q_heads,
                         softmax_scale, partition, workspace, workspace_bytes, out_dtype, out, err_count, stream, false,
                         k_new, v_new, slot_mapping);

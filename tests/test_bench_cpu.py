@@ -63,7 +63,7 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     src = os.path.join(ROOT, "quantized_paged_kv_absmax_amd", "csrc")
     dst = tmp_path / "quantized_paged_kv_absmax_amd" / "csrc"
     dst.mkdir(parents=True)
-    for f in ("decode_kernel.h", "decode.hip", "kvq_device.h"):
+    for f in ("decode_kernel.h", "decode.hip", "kvq_device.h", "kvq_rows.h"):
         shutil.copy(os.path.join(src, f), dst / f)
     h_repo = bench.decode_source_hash()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))

@@ -24,7 +24,7 @@ CASES = {
     "fp8_hybrid": dict(B=6),
     "fp8_e4m3_head": dict(B=6),
     "bf16": dict(B=6, lens=("uniform", 20, 700)),
-    "int4": dict(B=6, lens=("uniform", 20, 700)),     # INT4: the write, then the decode
+    "int4": dict(B=6, lens=("uniform", 20, 700)),     # INT4: the row encoder in the pre-pass
     "int4_had": dict(B=6, lens=("uniform", 20, 700)),
     "tiny_int8": dict(B=5, lens=("uniform", 1, 300)),  # head_dim 64, sequences of one token
 }
@@ -111,7 +111,7 @@ def test_one_call_equals_write_then_decode(name, partition):
         assert nbad == 0
 
 
-@pytest.mark.parametrize("name", ["llama8b_int8", "bf16", "tiny_int8"])
+@pytest.mark.parametrize("name", ["llama8b_int8", "bf16", "tiny_int8", "int4", "int4_had"])
 def test_slots_negative_out_of_pool_and_misplaced(name):
     """Sequence 0: slot -1 (neither call writes).  Sequence 1: the slot one past its
     last position on the same page, which attention never reads: the two calls
