@@ -86,8 +86,8 @@ struct Params {
   int n_q;           // query tokens per sequence (1: decode; more: the last n_q positions, causally)
   int n_tiles;       // 16-column MFMA tiles of the n_q * g rows of a (sequence, KV head)
   int wg_waves;      // several query tokens: waves (tiles) of a workgroup, which share its pages
-  // the step's new token, written in the same launch (one query token, 8- and
-  // 16-bit formats; null: none): bf16 rows [B][Hkv][D] and their slots [B]
+  // the step's new token, written in the same launch (one query token; null:
+  // none): bf16 rows [B][Hkv][D] and their slots [B]
   const uint16_t* new_k;
   const uint16_t* new_v;
   const int64_t* new_slot;
@@ -842,8 +842,7 @@ __global__ __launch_bounds__(MQ ? 256 : 64) void decode_chunk_kernel(Params p) {
   constexpr bool V_FOLD = (VT == DT_INT8 || VT == DT_INT4);
   constexpr float V_OFFSET = (VT == DT_INT8) ? 1152.0f : 128.0f;
   constexpr int KPAGE = KP::PAGE, VPAGE = VP::PAGE;
-  // the step's new token written in this launch: one query token, K and V in an
-  // 8- or 16-bit format (INT4 rows need a whole-row reduction first)
+  // the step's new token written in this launch (one query token)
   constexpr bool FW = NEW && !MQ;
   static_assert(!NEW || FW, "the new-token write: one query token");
   constexpr int STAGE_B = SG::STAGE;

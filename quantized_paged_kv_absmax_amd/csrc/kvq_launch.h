@@ -49,8 +49,8 @@ struct DecodeArgs {
   int out_f32;
   void* out;
   int32_t* err;
-  // one query token, 8- and 16-bit formats: the step's new token written in the
-  // same launch (rows [batch][Hkv][D] bf16, slots [batch]); NULL: none
+  // one query token: the step's new token written in the same launch (rows
+  // [batch][Hkv][D] bf16, slots [batch]); NULL: none
   const uint16_t* new_k = nullptr;
   const uint16_t* new_v = nullptr;
   const int64_t* new_slot = nullptr;
